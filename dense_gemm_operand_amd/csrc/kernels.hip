@@ -1,0 +1,710 @@
+// HIP kernels for gfx950 (CDNA4): C = A * B with operands in any row/column-major
+// layout, fp16/bf16 (or int4 B) in, fp32 accumulate, fp32/fp16/bf16 out.
+//
+// Tiled kernel, per workgroup and per K step of 64:
+//   1. 128-bit buffer loads of the A and B tiles into registers. A K-contiguous operand
+//      is read as whole 128-byte row segments; an operand whose contiguous index is M or
+//      N is read with consecutive lanes on consecutive 16-byte vectors along that index,
+//      each lane taking eight consecutive K rows of its vector (the "thread rake" of
+//      Triton PR 5223, item 2), so every load instruction covers whole 128-byte lines.
+//   2. In-register transpose of such an 8x8 block of 16-bit values with byte permutes
+//      (v_perm_b32; Triton PR 5223, "Feature description"), giving eight K-contiguous
+//      16-byte vectors, one per M/N index.
+//   3. 128-bit LDS stores into padded, row-permuted, K-contiguous tiles (lds_layout.hpp).
+//   4. 128-bit LDS reads of matrix-core fragments, v_mfma_f32_16x16x32_{f16,bf16}.
+//      Two LDS stages: the global loads of step t+1 are in flight while step t's
+//      fragments are multiplied; one barrier per step.
+//   5. Split-K across workgroups (BitBLAS PR 268, "SplitK Infer"; the K origin of split
+//      z is z * k_chunk): each split stores its fp32 partial tile; the last split to
+//      arrive at the tile's counter adds all partials in ascending split order.
+//   6. Epilogue: fp32 -> output type (round to nearest even), staged through LDS so
+//      that global stores are whole 16-byte row vectors.
+//
+// Skinny kernel (M <= 16, K-contiguous A and B, or int4 B): every wave of a workgroup
+// owns an interleaved share of the workgroup's K range and loads matrix-core fragments
+// straight from HBM; the waves' partial tiles are then reduced through LDS
+// (IREE PR 19596: partial reductions left across subgroups are re-distributed through
+// shared memory into element tiles and reduced again), then across workgroups as above.
+//
+// int4 B: 4-bit codes packed two per byte along K, (q - 8) * s rounded once to binary16
+// (BitBLAS PR 268, dequantize layout example with num_elems_per_byte = 2).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "lds_layout.hpp"
+#include "plan.hpp"
+
+namespace dg {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Buffer offset beyond every operand's num_records: such a load returns zeros.
+constexpr uint32_t kOOB = 0x80000000u;
+
+struct F16T {};
+struct BF16T {};
+
+template <class T>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c);
+template <>
+__device__ __forceinline__ f32x4 mfma16x16x32<F16T>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma16x16x32<BF16T>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  // Raw buffer (stride 0); word 3 = 32-bit data format, the gfx9-family default.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ uint16_t ld16b(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------- register transforms
+
+// 8x8 block of 16-bit values: in[kk] holds K row kk, elements e = 0..7 (two per dword,
+// element 2d in the low half of dword d). Out[e] holds element e for K rows 0..7 (K row
+// 2t in the low half of dword t). v_perm_b32 (D, S0, S1, sel): byte i of D is byte
+// sel.byte[i] of the 8-byte value S0:S1 (S1 = bytes 0..3). Selector 0x05040100 joins the
+// low halves of S1 and S0, 0x07060302 their high halves.
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      out[e][t] = __builtin_amdgcn_perm(in[2 * t + 1][e >> 1], in[2 * t][e >> 1], sel);
+  }
+}
+
+// Eight 4-bit codes of one dword (byte b: low nibble = code of K index 2b, high nibble =
+// code of 2b+1) -> eight binary16 weights (q - 8) * s, K-consecutive, as four dwords.
+// 0x6400 | q is the binary16 encoding of 1024 + q, so subtracting 1032 gives q - 8
+// exactly; the one rounding is the binary16 multiply by s.
+__device__ __forceinline__ u32x4 dequant8(uint32_t w, f16x2 s2) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+  const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  u32x4 r;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    // byte t of lo -> bits 0..7, byte t of hi -> bits 16..23, zeros elsewhere (sel 0x0C).
+    const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + t) << 16) | (uint32_t)t;
+    const uint32_t q2 = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
+    f16x2 v = __builtin_bit_cast(f16x2, q2) - bias;
+    v = v * s2;
+    r[t] = __builtin_bit_cast(uint32_t, v);
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------- output conversion
+
+template <int DT> struct OutT;
+template <> struct OutT<DT_F32> { using type = float; static constexpr int bytes = 4; };
+template <> struct OutT<DT_F16> { using type = _Float16; static constexpr int bytes = 2; };
+template <> struct OutT<DT_BF16> { using type = __bf16; static constexpr int bytes = 2; };
+
+template <int DT>
+__device__ __forceinline__ typename OutT<DT>::type cvt_out(float x) {
+  return (typename OutT<DT>::type)x;  // round to nearest even
+}
+
+// ---------------------------------------------------------------- kernel arguments
+
+struct KArgs {
+  const void* A;
+  const void* B;
+  const void* S;        // int4 scales (binary16, [K/128][N])
+  void* C;
+  float* part;          // fp32 partials (split-K), after the counters
+  int* counters;        // arrival counters (split-K)
+  int M, N, K;
+  int ldA, ldB;         // leading dimension of the stored operands
+  uint32_t bytesA, bytesB, bytesS;
+  int k_chunk;          // K per split (multiple of the K step)
+  int tiles_m, tiles_n;
+  int dtype_c;
+  int c_vec;            // 1 if every C row starts 16-byte aligned
+};
+
+// Split-K fix-up shared by both kernels. Every thread owns NV f32x4 partial vectors;
+// the workgroup stores them (coalesced, thread-major) into split z's slot, the last
+// workgroup to arrive at the tile's counter sums all splits in ascending order and
+// returns true; the others return false. The counter is reset for the next run.
+template <int NV, int THREADS>
+__device__ __forceinline__ bool splitk_fixup(f32x4 (&acc)[NV], const KArgs& a, int tile,
+                                             int z, int sk, int tiles) {
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
+  f32x4* base = reinterpret_cast<f32x4*>(a.part);
+  const size_t per_tile = (size_t)NV * THREADS;
+  f32x4* mine = base + ((size_t)z * tiles + tile) * per_tile;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) mine[(size_t)v * THREADS + tid] = acc[v];
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    const int old = __hip_atomic_fetch_add(a.counters + tile, 1, __ATOMIC_ACQ_REL,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (old == sk - 1);
+  }
+  __syncthreads();
+  if (!s_last) return false;
+  __threadfence();
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    f32x4 s = (z == 0) ? acc[v] : base[((size_t)0 * tiles + tile) * per_tile + (size_t)v * THREADS + tid];
+    for (int b = 1; b < sk; ++b) {
+      const f32x4 p = (b == z) ? acc[v]
+                               : base[((size_t)b * tiles + tile) * per_tile + (size_t)v * THREADS + tid];
+      s += p;
+    }
+    acc[v] = s;
+  }
+  if (tid == 0)
+    __hip_atomic_store(a.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+// ================================================================= tiled kernel
+
+template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN,
+          bool PERM>
+struct TileCfg {
+  static constexpr int BK = 64;
+  static constexpr int THREADS = WM * WN * 64;
+  static constexpr int WT_M = MT_M / WM, WT_N = MT_N / WN;
+  static constexpr int TM = WT_M / 16, TN = WT_N / 16;
+  static constexpr int PITCH = 9;  // LDS row pitch in 16-byte units: 128 B data + 16 B pad
+  static constexpr RowPerm PA = (!A_KC && PERM) ? RowPerm{64, 8} : RowPerm{1, 1};
+  static constexpr RowPerm PB = (!B_KC && !U4B && PERM) ? RowPerm{64, 8} : RowPerm{1, 1};
+  static constexpr int A16 = MT_M * PITCH, B16 = MT_N * PITCH;
+  static constexpr int STAGE16 = A16 + B16;
+  static constexpr int LDS_BYTES = 2 * STAGE16 * 16;
+  // Load units: eight 16-byte vectors each.
+  static constexpr int UA = MT_M * BK / 64;
+  static constexpr int UB = U4B ? MT_N * BK / 256 : MT_N * BK / 64;
+  static constexpr int NU = (UA + UB + THREADS - 1) / THREADS;
+  static_assert(WT_M % 16 == 0 && WT_N % 16 == 0, "wave tile must be whole 16x16 blocks");
+  static_assert(MT_M % 64 == 0 && MT_N % 64 == 0, "tile rows must be whole permutation blocks");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN,
+          bool PERM>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
+  using Cfg = TileCfg<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, PERM>;
+  constexpr int BK = Cfg::BK, THREADS = Cfg::THREADS, PITCH = Cfg::PITCH;
+  constexpr int TM = Cfg::TM, TN = Cfg::TN, NU = Cfg::NU, UA = Cfg::UA, UB = Cfg::UB;
+  constexpr RowPerm PA = Cfg::PA, PB = Cfg::PB;
+  __shared__ __attribute__((aligned(16))) u32x4 lds[Cfg::LDS_BYTES / 16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  // ---- tile index: XCD-aware remap (consecutive workgroup ids go round-robin over the
+  // 8 XCDs; give each XCD a contiguous range of tiles), then groups of 4 tile rows.
+  const int tiles = a.tiles_m * a.tiles_n;
+  int t = blockIdx.x;
+  if (tiles % 8 == 0) t = (t % 8) * (tiles / 8) + t / 8;
+  constexpr int GROUP_M = 4;
+  const int group = GROUP_M * a.tiles_n;
+  const int first_m = (t / group) * GROUP_M;
+  const int gsz = min(a.tiles_m - first_m, GROUP_M);
+  const int tile_m = first_m + (t % group) % gsz;
+  const int tile_n = (t % group) / gsz;
+  const int tile = tile_m * a.tiles_n + tile_n;
+  const int m0 = tile_m * MT_M, n0 = tile_n * MT_N;
+
+  const int z = blockIdx.z, sk = gridDim.z;
+  const int kb = z * a.k_chunk;
+  const int ke = min(a.K, kb + a.k_chunk);
+  const int nt = ke > kb ? (ke - kb + BK - 1) / BK : 0;
+
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.A, a.bytesA);
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.B, a.bytesB);
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.S, a.bytesS);
+
+  u32x4 raw[NU][8];
+  uint16_t sraw[NU][8];
+
+  // Issue the global loads of K step `step` into raw/sraw.
+  auto load_step = [&](int step) {
+    const int k0 = kb + step * BK;
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int u = i * THREADS + tid;
+      if (u < UA) {
+        if constexpr (A_KC) {
+          // unit u: vector j -> row j*MT_M/8 + u/8, 16-byte chunk u%8 of the K step
+          const int c = u % 8;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int r = j * (MT_M / 8) + u / 8;
+            const int gm = m0 + r, gk = k0 + 8 * c;
+            const bool ok = gm < a.M && gk < ke;
+            raw[i][j] = ld128(rA, ok ? (uint32_t)(gm * a.ldA + gk) * 2u : kOOB);
+          }
+        } else {
+          // unit u: vector v = u % (MT_M/8) along M, K rows 8*kg .. 8*kg+7
+          const int v = u % (MT_M / 8), kg = u / (MT_M / 8);
+          const int gm = m0 + 8 * v;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int gk = k0 + 8 * kg + j;
+            const bool ok = gm < a.M && gk < ke;
+            raw[i][j] = ld128(rA, ok ? (uint32_t)(gk * a.ldA + gm) * 2u : kOOB);
+          }
+        }
+      } else if (u < UA + UB) {
+        const int ub = u - UA;
+        if constexpr (U4B) {
+          // vector j of unit ub -> x = j*UB + ub: row x/2 (N index), K half x%2 (32 codes)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int x = j * UB + ub;
+            const int gn = n0 + x / 2, gk = k0 + 32 * (x % 2);
+            const bool ok = gn < a.N && gk < ke;
+            raw[i][j] = ld128(rB, ok ? (uint32_t)gn * (uint32_t)(a.K / 2) + (uint32_t)(gk / 2) : kOOB);
+            sraw[i][j] = ld16b(rS, ok ? ((uint32_t)(gk / 128) * (uint32_t)a.N + gn) * 2u : kOOB);
+          }
+        } else if constexpr (B_KC) {
+          const int c = ub % 8;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int r = j * (MT_N / 8) + ub / 8;
+            const int gn = n0 + r, gk = k0 + 8 * c;
+            const bool ok = gn < a.N && gk < ke;
+            raw[i][j] = ld128(rB, ok ? (uint32_t)(gn * a.ldB + gk) * 2u : kOOB);
+          }
+        } else {
+          const int v = ub % (MT_N / 8), kg = ub / (MT_N / 8);
+          const int gn = n0 + 8 * v;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int gk = k0 + 8 * kg + j;
+            const bool ok = gn < a.N && gk < ke;
+            raw[i][j] = ld128(rB, ok ? (uint32_t)(gk * a.ldB + gn) * 2u : kOOB);
+          }
+        }
+      }
+    }
+  };
+
+  // Transpose / dequantise the loaded registers and store them into LDS stage `st`.
+  auto store_step = [&](int st) {
+    u32x4* sA = lds + st * Cfg::STAGE16;
+    u32x4* sB = sA + Cfg::A16;
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int u = i * THREADS + tid;
+      if (u < UA) {
+        if constexpr (A_KC) {
+          const int c = u % 8;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int r = j * (MT_M / 8) + u / 8;
+            sA[PA.inv(r) * PITCH + c] = raw[i][j];
+          }
+        } else {
+          const int v = u % (MT_M / 8), kg = u / (MT_M / 8);
+          u32x4 tr[8];
+          transpose8x8(raw[i], tr);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sA[PA.inv(8 * v + e) * PITCH + kg] = tr[e];
+        }
+      } else if (u < UA + UB) {
+        const int ub = u - UA;
+        if constexpr (U4B) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int x = j * UB + ub;
+            const int r = x / 2, h = x % 2;
+            const _Float16 s = __builtin_bit_cast(_Float16, sraw[i][j]);
+            const f16x2 s2 = {s, s};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              sB[PB.inv(r) * PITCH + 4 * h + q] = dequant8(raw[i][j][q], s2);
+          }
+        } else if constexpr (B_KC) {
+          const int c = ub % 8;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int r = j * (MT_N / 8) + ub / 8;
+            sB[PB.inv(r) * PITCH + c] = raw[i][j];
+          }
+        } else {
+          const int v = ub % (MT_N / 8), kg = ub / (MT_N / 8);
+          u32x4 tr[8];
+          transpose8x8(raw[i], tr);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sB[PB.inv(8 * v + e) * PITCH + kg] = tr[e];
+        }
+      }
+    }
+  };
+
+  f32x4 acc[TM * TN];
+#pragma unroll
+  for (int i = 0; i < TM * TN; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Fragment reads: lane reads LDS row (16-row block base + lane%16), 16-byte chunk
+  // (lane/16) of the 32-K half step.
+  const int r16 = lane & 15, kc = lane >> 4;
+  const int a_rd = (wm * Cfg::WT_M + r16) * PITCH + kc;
+  const int b_rd = Cfg::A16 + (wn * Cfg::WT_N + r16) * PITCH + kc;
+
+  if (nt > 0) {
+    load_step(0);
+    store_step(0);
+  }
+  __syncthreads();
+  for (int s = 0; s < nt; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < nt) load_step(s + 1);
+    const u32x4* st = lds + cur * Cfg::STAGE16;
+#pragma unroll
+    for (int h = 0; h < BK / 32; ++h) {
+      u32x4 fa[TM], fb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[i] = st[a_rd + i * 16 * PITCH + 4 * h];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[j] = st[b_rd + j * 16 * PITCH + 4 * h];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i * TN + j] = mfma16x16x32<T>(fb[j], fa[i], acc[i * TN + j]);
+    }
+    if (s + 1 < nt) store_step(cur ^ 1);
+    __syncthreads();
+  }
+
+  if (sk > 1) {
+    if (!splitk_fixup<TM * TN, THREADS>(acc, a, tile, z, sk, tiles)) return;
+  }
+
+  // ---- epilogue: acc (i, j) block: lane holds logical row fwd_A(LDS row of lane%16) and
+  // the four logical columns fwd_B(LDS rows 4*(lane/16) + 0..3).
+  auto epilogue = [&](auto dt_tag) {
+    constexpr int DT = decltype(dt_tag)::value;
+    using O = typename OutT<DT>::type;
+    constexpr int OB = OutT<DT>::bytes;
+    constexpr int ROW_BYTES = MT_N * OB;
+    constexpr int CP = ROW_BYTES + 16;                    // LDS pitch of the C tile
+    constexpr int RPP0 = Cfg::LDS_BYTES / CP;
+    constexpr int RPP = RPP0 >= MT_M ? MT_M : (RPP0 / 16) * 16;  // rows per pass
+    constexpr int NPASS = (MT_M + RPP - 1) / RPP;
+    constexpr int CPR = ROW_BYTES / 16;                   // 16-byte chunks per row
+    char* cl = reinterpret_cast<char*>(lds);
+    O* Cg = reinterpret_cast<O*>(a.C);
+#pragma unroll 1
+    for (int p = 0; p < NPASS; ++p) {
+      const int lo = p * RPP;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int m = PA.fwd(wm * Cfg::WT_M + i * 16 + r16);
+        if (m < lo || m >= lo + RPP) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const f32x4 v = acc[i * TN + j];
+          const int nb = wn * Cfg::WT_N + j * 16 + 4 * kc;
+          if constexpr (PB.block == 1) {
+            O* dst = reinterpret_cast<O*>(cl + (m - lo) * CP + nb * OB);
+            typedef O o4 __attribute__((ext_vector_type(4)));
+            o4 w = {cvt_out<DT>(v[0]), cvt_out<DT>(v[1]), cvt_out<DT>(v[2]), cvt_out<DT>(v[3])};
+            *reinterpret_cast<o4*>(dst) = w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              O* dst = reinterpret_cast<O*>(cl + (m - lo) * CP + PB.fwd(nb + e) * OB);
+              *dst = cvt_out<DT>(v[e]);
+            }
+          }
+        }
+      }
+      __syncthreads();
+      const int rows = min(RPP, MT_M - lo);  // the last pass may be short
+      for (int c = tid; c < rows * CPR; c += THREADS) {
+        const int row = c / CPR, cc = c % CPR;
+        const int gm = m0 + lo + row;
+        const int gn = n0 + cc * (16 / OB);
+        if (gm >= a.M || gn >= a.N) continue;
+        const char* src = cl + row * CP + cc * 16;
+        if (a.c_vec && gn + 16 / OB <= a.N) {
+          *reinterpret_cast<u32x4*>(Cg + (size_t)gm * a.N + gn) = *reinterpret_cast<const u32x4*>(src);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 16 / OB; ++q)
+            if (gn + q < a.N) Cg[(size_t)gm * a.N + gn + q] = reinterpret_cast<const O*>(src)[q];
+        }
+      }
+      __syncthreads();
+    }
+  };
+  // The C tile reuses the operand LDS: every wave is past the loop's last barrier.
+  if (a.dtype_c == DT_F16) epilogue(std::integral_constant<int, DT_F16>{});
+  else if (a.dtype_c == DT_BF16) epilogue(std::integral_constant<int, DT_BF16>{});
+  else epilogue(std::integral_constant<int, DT_F32>{});
+}
+
+// ================================================================= skinny kernel
+
+// M <= 16, A row-major (K-contiguous), B column-major (K-contiguous) or int4 codes packed
+// along K. Workgroup: W waves over one 16 x (16*NB) output tile. A wave iteration covers
+// KI K indices: lane (r = lane%16, c = lane/16) loads, for B row n0+16*nb+r and A row r,
+// the K range [k + c*KI/4, k + (c+1)*KI/4); matrix-core step h uses the lane's h-th group
+// of eight K indices, identically for A and B, so the pairing of K indices is exact.
+template <class T, bool U4B, int NB, int W, int U>
+__global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
+  constexpr int THREADS = W * 64;
+  constexpr int KI = U4B ? 128 : 64;   // K per wave iteration
+  constexpr int H = KI / 32;           // matrix-core steps per iteration and n-block
+  constexpr int KL = KI / 4;           // K indices per lane per iteration
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, c = lane >> 4;
+  const int tile = blockIdx.x;
+  const int n0 = tile * 16 * NB;
+  const int z = blockIdx.y, sk = gridDim.y;
+  const int kb = z * a.k_chunk;
+  const int ke = min(a.K, kb + a.k_chunk);
+  const int n_it = ke > kb ? (ke - kb + KI - 1) / KI : 0;
+  const int my_n = n_it > wave ? (n_it - wave + W - 1) / W : 0;
+
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.A, a.bytesA);
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.B, a.bytesB);
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.S, a.bytesS);
+
+  constexpr int BV = U4B ? 1 : H;      // 16-byte B vectors per lane per n-block
+  u32x4 bufA[U][H];
+  u32x4 bufB[U][NB][BV];
+  uint16_t bufS[U][NB];
+
+  auto load = [&](int u, int j) {
+    const int it = wave + j * W;
+    const int k = kb + it * KI + c * KL;
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      const bool ok = r < a.M && k + 8 * h < ke;
+      bufA[u][h] = ld128(rA, ok ? (uint32_t)(r * a.ldA + k + 8 * h) * 2u : kOOB);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = n0 + 16 * nb + r;
+      if constexpr (U4B) {
+        const bool ok = n < a.N && k < ke;
+        bufB[u][nb][0] = ld128(rB, ok ? (uint32_t)n * (uint32_t)(a.K / 2) + (uint32_t)(k / 2) : kOOB);
+        bufS[u][nb] = ld16b(rS, ok ? ((uint32_t)(k / 128) * (uint32_t)a.N + n) * 2u : kOOB);
+      } else {
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+          const bool ok = n < a.N && k + 8 * h < ke;
+          bufB[u][nb][h] = ld128(rB, ok ? (uint32_t)(n * a.ldB + k + 8 * h) * 2u : kOOB);
+        }
+      }
+    }
+  };
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int u) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      if constexpr (U4B) {
+        const _Float16 s = __builtin_bit_cast(_Float16, bufS[u][nb]);
+        const f16x2 s2 = {s, s};
+#pragma unroll
+        for (int h = 0; h < H; ++h)
+          acc[nb] = mfma16x16x32<T>(dequant8(bufB[u][nb][0][h], s2), bufA[u][h], acc[nb]);
+      } else {
+#pragma unroll
+        for (int h = 0; h < H; ++h)
+          acc[nb] = mfma16x16x32<T>(bufB[u][nb][h], bufA[u][h], acc[nb]);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (u < my_n) load(u, u);
+  for (int j = 0; j < my_n; j += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (j + u < my_n) {
+        compute(u);
+        if (j + u + U < my_n) load(u, j + u + U);
+      }
+    }
+  }
+
+  // ---- cross-wave reduction through LDS: wave w's partial tile -> red[w]; then each
+  // thread sums, in wave order, the positions p = tid, tid + THREADS, ...
+  constexpr int P = NB * 64;                     // f32x4 positions per tile
+  constexpr int NV = (P + THREADS - 1) / THREADS;
+  __shared__ f32x4 red[W][P];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) red[wave][nb * 64 + lane] = acc[nb];
+  __syncthreads();
+  f32x4 sum[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int p = v * THREADS + tid;
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (p < P) {
+      s = red[0][p];
+#pragma unroll
+      for (int w = 1; w < W; ++w) s += red[w][p];
+    }
+    sum[v] = s;
+  }
+
+  if (sk > 1) {
+    if (!splitk_fixup<NV, THREADS>(sum, a, tile, z, sk, gridDim.x)) return;
+  }
+
+  // ---- store: position p = nb*64 + l holds row l%16, columns n0 + 16nb + 4(l/16) + 0..3
+  auto store = [&](auto dt_tag) {
+    constexpr int DT = decltype(dt_tag)::value;
+    using O = typename OutT<DT>::type;
+    O* Cg = reinterpret_cast<O*>(a.C);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int p = v * THREADS + tid;
+      if (p >= P) continue;
+      const int nb = p / 64, l = p % 64;
+      const int m = l & 15, n = n0 + 16 * nb + 4 * (l >> 4);
+      if (m >= a.M) continue;
+      O* dst = Cg + (size_t)m * a.N + n;
+      if (a.c_vec && n + 4 <= a.N) {
+        typedef O o4 __attribute__((ext_vector_type(4)));
+        o4 w = {cvt_out<DT>(sum[v][0]), cvt_out<DT>(sum[v][1]), cvt_out<DT>(sum[v][2]),
+                cvt_out<DT>(sum[v][3])};
+        *reinterpret_cast<o4*>(dst) = w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < a.N) dst[e] = cvt_out<DT>(sum[v][e]);
+      }
+    }
+  };
+  if (a.dtype_c == DT_F16) store(std::integral_constant<int, DT_F16>{});
+  else if (a.dtype_c == DT_BF16) store(std::integral_constant<int, DT_BF16>{});
+  else store(std::integral_constant<int, DT_F32>{});
+}
+
+// ================================================================= instantiation table
+
+using LaunchFn = hipError_t (*)(const Plan&, const KArgs&, hipStream_t);
+
+template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN, bool PERM>
+hipError_t launch_tile(const Plan& p, const KArgs& a, hipStream_t s) {
+  using Cfg = TileCfg<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, PERM>;
+  dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.grid_z);
+  hipLaunchKernelGGL((gemm_tile_kernel<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, PERM>), grid,
+                     dim3(Cfg::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+template <class T, bool U4B, int NB, int W, int U>
+hipError_t launch_skinny(const Plan& p, const KArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.grid_z);
+  hipLaunchKernelGGL((gemm_skinny_kernel<T, U4B, NB, W, U>), grid, dim3(W * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+template <class T> constexpr int dt_code() { return std::is_same<T, F16T>::value ? DT_F16 : DT_BF16; }
+
+struct Variant {
+  VariantInfo info;
+  LaunchFn fn;
+};
+
+#define TILE(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM)                                       \
+  Variant{VariantInfo{KERNEL_TILE, dt_code<T>(), (U4) ? DT_U4 : dt_code<T>(), (AKC) ? 0 : 1,  \
+                      (BKC) ? 1 : 0, MTM, MTN, 64, (WM) * (WN), 1, PERM,                     \
+                      TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM>::LDS_BYTES},          \
+          &launch_tile<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM>}
+
+#define TILE_LAYOUTS(T, MTM, MTN, WM, WN)                                                    \
+  TILE(T, true, true, false, MTM, MTN, WM, WN, true),                                      \
+  TILE(T, true, false, false, MTM, MTN, WM, WN, true),                                     \
+  TILE(T, false, true, false, MTM, MTN, WM, WN, true),                                     \
+  TILE(T, false, false, false, MTM, MTN, WM, WN, true)
+
+#define SKINNY(T, U4, NB, W, U)                                                              \
+  Variant{VariantInfo{KERNEL_SKINNY, dt_code<T>(), (U4) ? DT_U4 : dt_code<T>(), 0, 1, 16,     \
+                      16 * (NB), (U4) ? 128 : 64, W, W, 0, 0},                               \
+          &launch_skinny<T, U4, NB, W, U>}
+
+static const Variant kVariants[] = {
+    // skinny split-K kernels (M <= 16)
+    SKINNY(F16T, false, 4, 4, 2),
+    SKINNY(BF16T, false, 4, 4, 2),
+    SKINNY(F16T, true, 4, 4, 2),
+    // tiled kernels, every layout pair
+    TILE_LAYOUTS(F16T, 256, 256, 2, 4),
+    TILE_LAYOUTS(BF16T, 256, 256, 2, 4),
+    TILE_LAYOUTS(F16T, 192, 320, 2, 4),
+    TILE_LAYOUTS(BF16T, 192, 320, 2, 4),
+    TILE_LAYOUTS(F16T, 128, 128, 2, 2),
+    TILE_LAYOUTS(BF16T, 128, 128, 2, 2),
+    // int4 B (column-major codes), A either layout
+    TILE(F16T, true, true, true, 256, 256, 2, 4, true),
+    TILE(F16T, false, true, true, 256, 256, 2, 4, true),
+    TILE(F16T, true, true, true, 128, 128, 2, 2, true),
+    TILE(F16T, false, true, true, 128, 128, 2, 2, true),
+    // identity LDS row order (for comparisons of bank conflicts)
+    TILE(F16T, false, true, false, 256, 256, 2, 4, false),
+    TILE(F16T, true, false, false, 256, 256, 2, 4, false),
+};
+
+int variant_count() { return (int)(sizeof(kVariants) / sizeof(kVariants[0])); }
+const VariantInfo& variant_info(int i) { return kVariants[i].info; }
+
+int launch(const Plan& p, const RunArgs& r, void* stream) {
+  KArgs a;
+  a.A = r.A;
+  a.B = r.B;
+  a.S = r.scales;
+  a.C = r.C;
+  a.counters = reinterpret_cast<int*>(r.ws);
+  a.part = r.ws ? reinterpret_cast<float*>(reinterpret_cast<char*>(r.ws) + kCounterBytes) : nullptr;
+  a.M = (int)p.M;
+  a.N = (int)p.N;
+  a.K = (int)p.K;
+  a.ldA = (int)(p.layout_a == 0 ? p.K : p.M);
+  a.ldB = (int)(p.layout_b == 0 ? p.N : p.K);
+  const int eb_b = p.dtype_b == DT_U4 ? 1 : 2;
+  a.bytesA = (uint32_t)(p.M * p.K * 2);
+  a.bytesB = (uint32_t)(p.dtype_b == DT_U4 ? p.N * p.K / 2 : p.N * p.K * eb_b);
+  a.bytesS = (uint32_t)(p.dtype_b == DT_U4 ? (p.K / 128) * p.N * 2 : 0);
+  a.k_chunk = (int)p.k_chunk;
+  a.tiles_m = (int)((p.M + p.tile_m - 1) / p.tile_m);
+  a.tiles_n = (int)((p.N + p.tile_n - 1) / p.tile_n);
+  a.dtype_c = p.dtype_c;
+  const int ob = p.dtype_c == DT_F32 ? 4 : 2;
+  a.c_vec = ((p.N * ob) % 16 == 0) ? 1 : 0;
+  if (p.kernel == KERNEL_SKINNY) a.c_vec = (p.N % 4 == 0) ? 1 : 0;  // 4-element stores
+  return (int)kVariants[p.variant].fn(p, a, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // namespace dg

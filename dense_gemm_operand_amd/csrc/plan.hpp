@@ -1,0 +1,63 @@
+// Internal plan record shared by the planner, the ABI layer and the kernel launchers.
+#pragma once
+#include <cstdint>
+
+namespace dg {
+
+enum Kernel : int32_t { KERNEL_TILE = 0, KERNEL_SKINNY = 1 };
+
+// Element-type codes (same numbering as the public header).
+enum Dtype : int32_t { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_U4 = 3 };
+
+struct Plan {
+  int64_t M = 0, N = 0, K = 0;
+  int32_t layout_a = 0, layout_b = 0;  // 0 row-major, 1 column-major
+  int32_t dtype_a = 0, dtype_b = 0, dtype_c = 0;
+  int32_t kernel = KERNEL_TILE;
+  int32_t variant = -1;                // index into the launcher's instantiation table
+  int32_t tile_m = 0, tile_n = 0, tile_k = 0;
+  int32_t waves = 0;
+  int32_t lds_pad = 0, perm_block = 1, perm_stride = 1;
+  int32_t split_k = 1;                 // across workgroups
+  int32_t wave_split_k = 1;            // across waves of a workgroup
+  int64_t k_chunk = 0;                 // K elements per split (multiple of the step)
+  int64_t grid_x = 0, grid_y = 0, grid_z = 0;
+  int64_t tiles = 0;                   // output tiles (= counters used when split_k > 1)
+  int64_t partial_bytes_per_split = 0; // fp32 partial bytes of one split
+  int64_t workspace_bytes = 0;
+  int32_t lds_bytes = 0;
+  int32_t cu_count = 0;
+  int32_t device = -1;
+};
+
+// Arrival counters occupy the first kCounterBytes of every workspace.
+constexpr int64_t kCounterBytes = 64 * 1024;
+constexpr int64_t kMaxCounters = kCounterBytes / 4;
+
+// Device pointers and sizes for one run.
+struct RunArgs {
+  const void* A;
+  const void* B;
+  const void* scales;
+  void* C;
+  void* ws;
+};
+
+// Instantiation table of the launcher (kernels.hip).
+struct VariantInfo {
+  int32_t kernel;
+  int32_t dtype_a, dtype_b;       // DT_F16/DT_BF16; dtype_b DT_U4 for int4
+  int32_t layout_a, layout_b;     // required layouts
+  int32_t tile_m, tile_n, tile_k;
+  int32_t waves;
+  int32_t wave_split_k;
+  int32_t perm;                   // 1 = permuted LDS rows for transposed operands
+  int32_t lds_bytes;
+};
+
+int variant_count();
+const VariantInfo& variant_info(int i);
+// Returns 0 or a hipError_t value.
+int launch(const Plan& p, const RunArgs& a, void* stream);
+
+}  // namespace dg

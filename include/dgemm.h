@@ -1,0 +1,143 @@
+/*
+ * dgemm.h -- C ABI of the MI355X (gfx950) operand-layout GEMM library (libdgemm.so).
+ *
+ * The library computes C = A * B on one GPU, where the logical A is M x K, the logical B
+ * is K x N and either operand may be stored row- or column-major. An operand whose K
+ * index is not the contiguous one (a "non-TN" operand: Triton PR 5223, "Feature
+ * description", where such operands are called K-major / non-KContig) is read with
+ * 128-bit coalesced loads, transposed in registers and stored K-contiguous in LDS, so
+ * the matrix-core loop always reads K-contiguous fragments. Skinny shapes split K
+ * (BitBLAS PR 268, "SplitK Infer") and reduce the partial sums first across the
+ * wavefronts of a workgroup through LDS (IREE PR 19596, inter-subgroup reduction
+ * description), then across workgroups. B may instead be 4-bit weight codes with
+ * per-group binary16 scales that the loader dequantises (BitBLAS PR 268, dequantize
+ * layout example).
+ *
+ * Conventions for every entry point:
+ *   - Return value 0 (GEMM_OK) on success, a negative GEMM_ERR_* code otherwise.
+ *   - No entry point aborts, throws across the ABI, prints (unless the environment
+ *     variable DGEMM_DEBUG is set) or synchronises the device.
+ *   - All argument checks happen before any GPU work is enqueued.
+ *   - The library never allocates or frees device memory; the caller owns every device
+ *     buffer. The only library-owned object is the host-side plan.
+ */
+#ifndef DGEMM_H
+#define DGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage order of a logical matrix (A is M x K, B is K x N). Row-major: element (r, c)
+ * at r * cols + c. Column-major: element (r, c) at r + c * rows. Storage is packed (no
+ * leading dimension). */
+enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1 };
+
+/* Element types. GEMM_U4 is valid for B only: two 4-bit codes per byte along K. */
+enum { GEMM_F32 = 0, GEMM_F16 = 1, GEMM_BF16 = 2, GEMM_U4 = 3 };
+
+/* Status codes. */
+enum {
+  GEMM_OK = 0,
+  GEMM_ERR_INVALID_ARG = -1,         /* null pointer, bad enum, non-positive size */
+  GEMM_ERR_UNSUPPORTED = -2,         /* valid request this library does not implement */
+  GEMM_ERR_MISALIGNED = -3,          /* a device pointer is not 16-byte aligned */
+  GEMM_ERR_WORKSPACE_TOO_SMALL = -4, /* ws_bytes below gemm_workspace_size() */
+  GEMM_ERR_NO_DEVICE = -5,           /* no usable HIP device / wrong device current */
+  GEMM_ERR_HIP = -6                  /* a HIP runtime call or kernel launch failed */
+};
+
+/* Quantisation of an int4 B operand (BitBLAS PR 268, dequantize layout example:
+ * num_elems_per_byte = 2). Weight w(k, n) = round_fp16((q(k, n) - zero_point) * s).
+ * q(k, n) is the low nibble of byte n*(K/2) + k/2 for even k, the high nibble for odd k.
+ * s = scales[(k / group_size) * N + n], binary16. Only group_size = 128, zero_point = 8,
+ * scale_dtype = GEMM_F16 and scale_layout = 0 ([K/group][N] row-major) are supported. */
+typedef struct {
+  int32_t group_size;
+  int32_t zero_point;
+  int32_t scale_dtype;
+  int32_t scale_layout;
+} gemm_quant_t;
+
+/* Opaque host-side plan. Immutable once made; usable from several streams at once if
+ * each concurrent run has its own workspace. */
+typedef struct gemm_plan_s* gemm_plan_t;
+
+/* What the planner chose (for reports and tests). */
+typedef struct {
+  int64_t M, N, K;
+  int32_t layout_a, layout_b, dtype_a, dtype_b, dtype_c;
+  int32_t kernel;          /* 0 = tiled kernel, 1 = skinny split-K kernel */
+  int32_t tile_m, tile_n, tile_k; /* macro tile; tile_k = K elements per main-loop step */
+  int32_t waves;           /* wavefronts (64 lanes) per workgroup */
+  int32_t lds_pad_bytes;   /* padding after each K-contiguous LDS row */
+  int32_t perm_block;      /* rows per block of the LDS row permutation (1 = none) */
+  int32_t perm_stride;     /* stride S of that permutation (rocm-libraries PR 2487) */
+  int32_t split_k;         /* K splits across workgroups */
+  int32_t wave_split_k;    /* K splits across the waves of one workgroup (1 = none) */
+  int64_t grid_x, grid_y, grid_z;
+  int64_t workspace_bytes; /* what gemm_run needs (0 when split_k == 1) */
+  int32_t lds_bytes;       /* LDS per workgroup */
+  int32_t cu_count;        /* compute units the split-K search assumed */
+} gemm_plan_info_t;
+
+/* Make a plan for C (M x N, row-major, dtype_c) = A (M x K) * B (K x N).
+ *
+ * layout_a/layout_b: GEMM_ROW_MAJOR or GEMM_COL_MAJOR storage of the logical operands.
+ * dtype_a: GEMM_F16 or GEMM_BF16. dtype_b: the same as dtype_a, or GEMM_U4 with
+ *   dtype_a == GEMM_F16, layout_b == GEMM_COL_MAJOR (codes packed along K) and a
+ *   non-null `quant` (otherwise quant must be NULL or is ignored).
+ * dtype_c: GEMM_F32, GEMM_F16 or GEMM_BF16 (round-to-nearest-even from fp32 sums).
+ * split_k: 0 lets the planner choose (waste-ratio search over the CU count, BitBLAS
+ *   PR 268 "SplitK Infer", capped at 16); otherwise 1, 2, 4, 8 or 16.
+ * Constraints: M, N, K >= 1; the contiguous extent of each operand is a multiple of 8
+ *   elements (K for row-major A and column-major B, M for column-major A, N for
+ *   row-major B); int4 needs K % 128 == 0. Violations give GEMM_ERR_UNSUPPORTED.
+ * The plan binds to the HIP device current at this call (its CU count feeds the
+ * split-K search; the environment variable DGEMM_FAKE_CU_COUNT replaces the query so
+ * that planning works without a device). Host only: no allocation, no launch.
+ * On error *out is set to NULL. */
+int gemm_plan(gemm_plan_t* out, int64_t M, int64_t N, int64_t K, int layout_a, int layout_b,
+              int dtype_a, int dtype_b, int dtype_c, int split_k, const gemm_quant_t* quant);
+
+/* Bytes of device workspace gemm_run needs for this plan (0 when split_k == 1). */
+int gemm_workspace_size(gemm_plan_t plan, size_t* bytes);
+
+/* Enqueue C = A * B on `stream` (a hipStream_t; NULL is the default stream) and return
+ * without synchronising.
+ * A, B, C (and scales for int4 B) are device pointers in the plan's layouts, each
+ * 16-byte aligned; C must not alias A, B or scales. workspace (16-byte aligned,
+ * ws_bytes >= gemm_workspace_size) is needed when split_k > 1, else may be NULL.
+ * Workspace contract: its first 64 KiB hold arrival counters that must be zero before
+ * the workspace is first used; every run that completes leaves them zero again, so a
+ * workspace zeroed once can be reused by any plan. Runs that share a workspace must
+ * not overlap in time. The rest of the workspace is scratch.
+ * Summation order is fixed (split partial sums are added in ascending split index), so
+ * repeated runs give identical bits. */
+int gemm_run(gemm_plan_t plan, const void* A, const void* B, const void* scales, void* C,
+             void* workspace, size_t ws_bytes, void* stream);
+
+/* Copy the planner's choices into *info. */
+int gemm_plan_query(gemm_plan_t plan, gemm_plan_info_t* info);
+
+/* Free a plan (NULL is ignored). */
+void gemm_plan_destroy(gemm_plan_t plan);
+
+/* Static text for a status code. */
+const char* gemm_status_string(int status);
+
+/* Row permutation used inside LDS tiles (rocm-libraries PR 2487, "Add support for
+ * permuting perpDim"): with S' = B / S, forward I' = S*(I mod S') + I / S' and inverse
+ * I = S'*(I' mod S) + I' / S. Returns the image of `index` (0 <= index < block) under the
+ * forward map (inverse != 0: the inverse map), or -1 when S does not divide B or an
+ * argument is out of range. Host-side view of the same function the kernels use. */
+int gemm_lds_row_perm(int block, int stride, int index, int inverse);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DGEMM_H */

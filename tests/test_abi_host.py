@@ -1,0 +1,183 @@
+"""Host-side tests of libdgemm (no GPU): the library loads and exports every entry point
+of include/dgemm.h, plans validate their arguments, the planner's split-K search and LDS
+row permutation agree with the oracle's reading of the pages, and gemm_run rejects bad
+arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import dense_gemm_operand_amd as dg
+import oracle
+from helpers import env
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dgemm.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared_functions() == sorted([
+        "gemm_plan", "gemm_workspace_size", "gemm_run", "gemm_plan_query",
+        "gemm_plan_destroy", "gemm_status_string", "gemm_lds_row_perm"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(dg.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for st in range(-6, 1):
+        assert dg.gemm_status_string(st) not in ("", "unknown status")
+    assert dg.gemm_status_string(-99) == "unknown status"
+
+
+def _plan_status(*args, quant=None):
+    h = ctypes.c_void_p()
+    q = ctypes.byref(quant) if quant is not None else None
+    st = dg.lib().gemm_plan(ctypes.byref(h), *args, q)
+    if h.value:
+        dg.gemm_plan_destroy(h.value)
+    return st, h.value
+
+
+F16, BF16, U4, F32 = dg.GEMM_F16, dg.GEMM_BF16, dg.GEMM_U4, dg.GEMM_F32
+ROW, COL = dg.GEMM_ROW_MAJOR, dg.GEMM_COL_MAJOR
+
+
+@pytest.fixture
+def fake_cus():
+    with env(DGEMM_FAKE_CU_COUNT=256):
+        yield
+
+
+def test_plan_argument_errors(fake_cus):
+    ok = (64, 64, 64, ROW, COL, F16, F16, F16, 0)
+    assert _plan_status(*ok)[0] == dg.GEMM_OK
+    bad = [
+        ((0, 64, 64, ROW, COL, F16, F16, F16, 0), dg.GEMM_ERR_INVALID_ARG),
+        ((64, -1, 64, ROW, COL, F16, F16, F16, 0), dg.GEMM_ERR_INVALID_ARG),
+        ((64, 64, 64, 2, COL, F16, F16, F16, 0), dg.GEMM_ERR_INVALID_ARG),
+        ((64, 64, 64, ROW, COL, 7, F16, F16, 0), dg.GEMM_ERR_INVALID_ARG),
+        ((64, 64, 64, ROW, COL, F16, F16, F16, -1), dg.GEMM_ERR_INVALID_ARG),
+        ((64, 64, 64, ROW, COL, F16, F16, F16, 3), dg.GEMM_ERR_UNSUPPORTED),
+        ((64, 64, 64, ROW, COL, F16, F16, F16, 32), dg.GEMM_ERR_UNSUPPORTED),
+        ((64, 64, 64, ROW, COL, F16, BF16, F16, 0), dg.GEMM_ERR_UNSUPPORTED),   # mixed
+        ((64, 64, 64, ROW, COL, F32, F32, F32, 0), dg.GEMM_ERR_UNSUPPORTED),    # fp32 in
+        ((64, 64, 60, ROW, COL, F16, F16, F16, 0), dg.GEMM_ERR_UNSUPPORTED),    # K % 8
+        ((60, 64, 64, COL, COL, F16, F16, F16, 0), dg.GEMM_ERR_UNSUPPORTED),    # M % 8, col A
+        ((64, 60, 64, ROW, ROW, F16, F16, F16, 0), dg.GEMM_ERR_UNSUPPORTED),    # N % 8, row B
+        ((64, 64, 64, ROW, COL, F16, U4, F16, 0), dg.GEMM_ERR_UNSUPPORTED),     # u4 w/o quant
+        ((64, 64, 64, ROW, COL, F16, F16, U4, 0), dg.GEMM_ERR_UNSUPPORTED),     # u4 output
+    ]
+    for args, want in bad:
+        assert _plan_status(*args)[0] == want, args
+    q = dg.int4_quant()
+    assert _plan_status(64, 64, 256, ROW, COL, F16, U4, F16, 0, quant=q)[0] == dg.GEMM_OK
+    assert _plan_status(64, 64, 200, ROW, COL, F16, U4, F16, 0, quant=q)[0] == dg.GEMM_ERR_UNSUPPORTED
+    assert _plan_status(64, 64, 256, ROW, ROW, F16, U4, F16, 0, quant=q)[0] == dg.GEMM_ERR_UNSUPPORTED
+    assert _plan_status(64, 64, 256, ROW, COL, BF16, U4, F16, 0, quant=q)[0] == dg.GEMM_ERR_UNSUPPORTED
+    q2 = dg.gemm_quant_t(64, 8, F16, 0)
+    assert _plan_status(64, 64, 256, ROW, COL, F16, U4, F16, 0, quant=q2)[0] == dg.GEMM_ERR_UNSUPPORTED
+    # M <= 16 with non-contiguous extents that are not multiples of 8 stay allowed where
+    # the contiguous index is K
+    assert _plan_status(3, 5, 64, ROW, COL, F16, F16, F16, 0)[0] == dg.GEMM_OK
+
+
+def test_plan_without_device_is_no_device():
+    with env(DGEMM_FAKE_CU_COUNT=None, HIP_VISIBLE_DEVICES=None):
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a device is present")
+        assert _plan_status(64, 64, 64, ROW, COL, F16, F16, F16, 0)[0] == dg.GEMM_ERR_NO_DEVICE
+
+
+@pytest.mark.parametrize("M,N,K,la,lb,dt,db", [
+    (16, 8192, 28672, ROW, COL, F16, F16),
+    (16, 8192, 8192, ROW, COL, F16, U4),
+    (16, 1000, 4096, ROW, COL, BF16, BF16),
+    (4096, 4096, 4096, COL, COL, F16, F16),
+    (3072, 5120, 6144, COL, ROW, BF16, BF16),
+    (256, 256, 256, ROW, ROW, F16, F16),
+    (100, 3000, 50000, ROW, ROW, F16, F16),
+])
+def test_split_k_choice_matches_the_page_search(fake_cus, M, N, K, la, lb, dt, db):
+    q = dg.int4_quant() if db == U4 else None
+    p = dg.gemm_plan(M, N, K, la, lb, dt, db, F16, 0, q)
+    info = dg.gemm_plan_query(p)
+    dg.gemm_plan_destroy(p)
+    step = info["tile_k"] * (info["waves"] if info["kernel"] == 1 else 1)
+    want = oracle.splitk_factor(M, N, K, info["tile_m"], info["tile_n"], step, 256)
+    assert info["split_k"] == want
+    tiles = -(-M // info["tile_m"]) * -(-N // info["tile_n"])
+    assert info["grid_x"] * info["grid_y"] * info["grid_z"] == tiles * want
+    if want > 1:
+        assert info["workspace_bytes"] >= dg.COUNTER_BYTES + want * tiles * info["tile_m"] * info["tile_n"] * 4
+    else:
+        assert info["workspace_bytes"] == 0
+
+
+def test_headline_plans(fake_cus):
+    p = dg.gemm_plan(4096, 4096, 4096, COL, COL, F16, F16, F16, 0)
+    i = dg.gemm_plan_query(p)
+    dg.gemm_plan_destroy(p)
+    assert (i["tile_m"], i["tile_n"], i["split_k"], i["grid_x"]) == (256, 256, 1, 256)
+    assert (i["perm_block"], i["perm_stride"], i["lds_pad_bytes"]) == (64, 8, 16)
+    assert i["lds_bytes"] <= 160 * 1024
+    p = dg.gemm_plan(3072, 5120, 6144, COL, ROW, BF16, BF16, BF16, 0)
+    i = dg.gemm_plan_query(p)
+    dg.gemm_plan_destroy(p)
+    assert (i["tile_m"], i["tile_n"], i["grid_x"]) == (192, 320, 256)   # non-power-of-2 tile
+
+
+def test_lds_row_permutation_matches_the_page_formula():
+    for B in range(1, 257):
+        for S in range(1, B + 1):
+            if B % S:
+                assert dg.gemm_lds_row_perm(B, S, 0, False) == -1
+                continue
+            f = [dg.gemm_lds_row_perm(B, S, i, False) for i in range(B)]
+            assert f == [oracle.perm_fwd(i, B, S) for i in range(B)]
+            assert [dg.gemm_lds_row_perm(B, S, x, True) for x in f] == list(range(B))
+    assert dg.gemm_lds_row_perm(8, 2, 8, False) == -1
+
+
+def test_run_rejects_bad_arguments_before_any_device_work(fake_cus):
+    p = dg.gemm_plan(128, 128, 4096, ROW, COL, F16, F16, F16, 4)
+    try:
+        need = dg.gemm_workspace_size(p)
+        assert need > 0
+        L = dg.lib()
+        A, B, C, W = 0x10000, 0x20000, 0x30000, 0x40000   # never dereferenced
+        assert L.gemm_run(None, A, B, None, C, W, need, None) == dg.GEMM_ERR_INVALID_ARG
+        assert L.gemm_run(p, None, B, None, C, W, need, None) == dg.GEMM_ERR_INVALID_ARG
+        assert L.gemm_run(p, A + 8, B, None, C, W, need, None) == dg.GEMM_ERR_MISALIGNED
+        assert L.gemm_run(p, A, B, None, C + 2, W, need, None) == dg.GEMM_ERR_MISALIGNED
+        assert L.gemm_run(p, A, B, None, C, None, need, None) == dg.GEMM_ERR_INVALID_ARG
+        assert L.gemm_run(p, A, B, None, C, W, need - 16, None) == dg.GEMM_ERR_WORKSPACE_TOO_SMALL
+        assert L.gemm_run(p, A, B, None, C, W + 4, need, None) == dg.GEMM_ERR_MISALIGNED
+        # a plan made without a device cannot run
+        assert L.gemm_run(p, A, B, None, C, W, need, None) == dg.GEMM_ERR_NO_DEVICE
+    finally:
+        dg.gemm_plan_destroy(p)
+    q = dg.int4_quant()
+    p = dg.gemm_plan(16, 128, 256, ROW, COL, F16, U4, F16, 1, q)
+    try:
+        assert dg.lib().gemm_run(p, 0x10000, 0x20000, None, 0x30000, None, 0, None) == dg.GEMM_ERR_INVALID_ARG
+    finally:
+        dg.gemm_plan_destroy(p)
+
+
+def test_query_and_destroy_null():
+    assert dg.lib().gemm_plan_query(None, None) == dg.GEMM_ERR_INVALID_ARG
+    assert dg.lib().gemm_workspace_size(None, None) == dg.GEMM_ERR_INVALID_ARG
+    dg.gemm_plan_destroy(None)

@@ -1,0 +1,187 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Integer-valued inputs make every partial sum exact in fp32, so the GPU result must equal
+the oracle bit for bit whatever the layout, tile, permutation or split; random inputs
+must meet the acceptance bar (relative Frobenius <= 1e-3 against the oracle rounded to
+the output format, every element within 4e-3 * sqrt(K) * max|a| * max|b|)."""
+import numpy as np
+import pytest
+
+import oracle
+from dense_gemm_operand_amd import synth
+from helpers import check_tolerance, operand_max, reference, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = [("row", "row"), ("row", "col"), ("col", "row"), ("col", "col")]
+TILES = ["256x256", "192x320", "128x128"]
+
+
+def _inputs_int(M, N, K, la, lb, fmt, seed, lo=-2, hi=2):
+    rng = np.random.default_rng(seed)
+    a = synth.integer_matrix(rng, M, K, lo, hi, fmt)
+    b = synth.integer_matrix(rng, K, N, lo, hi, fmt)
+    return {"M": M, "N": N, "K": K, "layout_a": la, "layout_b": lb,
+            "A": synth.store(a, la), "B": synth.store(b, lb)}
+
+
+def _inputs_rand(M, N, K, la, lb, fmt, seed, dist="normal_sqrtk"):
+    w = synth.Workload("t", 0, M, N, K, la, lb, fmt, fmt, dist)
+    return synth.make_inputs(w, seed=seed)
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_integer_inputs_bit_exact_every_layout_and_tile(tile, la, lb, fmt):
+    # several tiles in each direction plus ragged tails in M, N and K
+    M, N, K = 392 + 8, 648, 200
+    _say("int", tile, la, lb, fmt, M, N, K)
+    inp = _inputs_int(M, N, K, la, lb, fmt, seed=21)
+    c, info = run_gpu(inp, fmt, "f32", split_k=1, force_tile=tile, guard=64)
+    assert f"{info['tile_m']}x{info['tile_n']}" == tile
+    _, ref = reference(inp, fmt, "f32")
+    assert np.array_equal(c, ref)
+
+
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+@pytest.mark.parametrize("fmt,out", [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"),
+                                     ("bf16", "f32"), ("f16", "bf16")])
+def test_random_inputs_within_tolerance(la, lb, fmt, out):
+    M, N, K = 520, 392, 328
+    _say("rand", la, lb, fmt, out)
+    inp = _inputs_rand(M, N, K, la, lb, fmt, seed=31)
+    c, _ = run_gpu(inp, fmt, out, split_k=1, guard=32)
+    _, ref = reference(inp, fmt, out)
+    amax, bmax = operand_max(inp, fmt)
+    check_tolerance(c, ref, out, K, amax, bmax, f"{la}/{lb} {fmt}->{out}")
+
+
+@pytest.mark.parametrize("sk", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("la,lb", [("row", "row"), ("col", "col")])
+def test_split_k_integer_identical_for_every_factor(sk, la, lb):
+    M, N, K = 264, 136, 1096
+    _say("splitk-tile", sk, la, lb)
+    inp = _inputs_int(M, N, K, la, lb, "f16", seed=41, lo=-3, hi=3)
+    c, info = run_gpu(inp, "f16", "f32", split_k=sk, force_tile="128x128", guard=16)
+    assert info["split_k"] == sk
+    _, ref = reference(inp, "f16", "f32")
+    assert np.array_equal(c, ref)
+
+
+def test_split_k_random_deterministic_and_within_tolerance():
+    M, N, K = 304, 200, 4000
+    _say("splitk-determinism")
+    inp = _inputs_rand(M, N, K, "col", "row", "bf16", seed=42, dist="normal002")
+    outs, info = run_gpu(inp, "bf16", "bf16", split_k=8, repeat=3, force_tile="128x128")
+    assert info["split_k"] == 8
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+    _, ref = reference(inp, "bf16", "bf16")
+    amax, bmax = operand_max(inp, "bf16")
+    check_tolerance(outs[0], ref, "bf16", K, amax, bmax, "split-K bf16")
+
+
+def test_split_k_with_empty_splits():
+    # K = 256 in 16 splits of 64: four splits hold all of K, twelve are empty
+    M, N, K = 128, 128, 256
+    _say("empty-splits")
+    inp = _inputs_int(M, N, K, "row", "row", "f16", seed=43)
+    c, info = run_gpu(inp, "f16", "f32", split_k=16, force_tile="128x128")
+    _, ref = reference(inp, "f16", "f32")
+    assert np.array_equal(c, ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 8192 // 8, 28672 // 8), (1, 200, 4104), (4, 1, 4096),
+                                   (1, 1, 4096), (13, 24, 264)])
+@pytest.mark.parametrize("sk", [0, 1, 4])
+def test_skinny_integer_bit_exact(M, N, K, sk):
+    _say("skinny-int", M, N, K, sk)
+    inp = _inputs_int(M, N, K, "row", "col", "f16", seed=51, lo=-4, hi=4)
+    c, info = run_gpu(inp, "f16", "f32", split_k=sk, guard=8)
+    assert info["kernel"] == 1
+    _, ref = reference(inp, "f16", "f32")
+    assert np.array_equal(c, ref)
+
+
+def test_reduction_shapes_of_the_cross_wave_reduce():
+    # 4096 -> 1 and 4 x 4096 -> 4 sums (IREE PR 19596 test cases) as products with ones
+    for M in (1, 4):
+        _say("reduce", M)
+        rng = np.random.default_rng(52 + M)
+        a = synth.integer_matrix(rng, M, 4096, -8, 8, "f16")
+        ones = synth.to_bits(np.ones((4096, 1)), "f16")
+        inp = {"M": M, "N": 1, "K": 4096, "layout_a": "row", "layout_b": "col",
+               "A": synth.store(a, "row"), "B": synth.store(ones, "col")}
+        c, info = run_gpu(inp, "f16", "f32", split_k=0)
+        want = oracle.decode(a, "f16").sum(axis=1)
+        assert np.array_equal(oracle.decode(c, "f32")[:, 0], want)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_skinny_random_within_tolerance(fmt):
+    M, N, K = 16, 1024, 7168
+    _say("skinny-rand", fmt)
+    inp = _inputs_rand(M, N, K, "row", "col", fmt, seed=53, dist="uniform05")
+    c, info = run_gpu(inp, fmt, fmt, split_k=0)
+    _, ref = reference(inp, fmt, fmt)
+    amax, bmax = operand_max(inp, fmt)
+    check_tolerance(c, ref, fmt, K, amax, bmax, "skinny")
+
+
+def _int4_inputs(M, N, K, seed, la="row"):
+    w = synth.WORKLOADS["int4_m16"]
+    inp = synth.make_inputs(w, M=M, N=N, K=K, seed=seed, layout_a=la)
+    return inp
+
+
+@pytest.mark.parametrize("M", [16, 256])
+def test_int4_dequant_bit_exact_through_identity_rows(M):
+    # A = unit rows picking K indices, so C rows are dequantised weight rows, exactly
+    N, K = 320, 512
+    _say("int4-identity", M)
+    inp = _int4_inputs(M, N, K, seed=61)
+    pick = np.random.default_rng(62).choice(K, size=M, replace=False)
+    a = np.zeros((M, K))
+    a[np.arange(M), pick] = 1.0
+    inp["A"] = synth.store(synth.to_bits(a, "f16"), "row")
+    c, info = run_gpu(inp, "f16", "f16", split_k=1, int4=True)
+    w = oracle.dequant_u4(inp["B"], inp["scales"], K, N)
+    assert np.array_equal(oracle.decode(c, "f16"), w[pick])
+
+
+@pytest.mark.parametrize("M,la", [(16, "row"), (8, "row"), (384, "row"), (384, "col")])
+def test_int4_random_within_tolerance(M, la):
+    N, K = 512, 1024
+    _say("int4-rand", M, la)
+    inp = _int4_inputs(M, N, K, seed=63, la=la)
+    c, info = run_gpu(inp, "f16", "f16", split_k=0, int4=True, guard=8)
+    _, ref = reference(inp, "f16", "f16", int4=True)
+    amax, bmax = operand_max(inp, "f16", int4=True)
+    check_tolerance(c, ref, "f16", K, amax, bmax, "int4")
+
+
+def test_no_permutation_variant_matches():
+    # the identity-row-order variant gives the same bits as the permuted one
+    M, N, K = 512, 512, 256
+    _say("perm-off")
+    inp = _inputs_int(M, N, K, "col", "col", "f16", seed=71)
+    from helpers import env
+    with env(DGEMM_NO_PERM=1):
+        c0, i0 = run_gpu(inp, "f16", "f32", split_k=1, force_tile="256x256")
+    c1, i1 = run_gpu(inp, "f16", "f32", split_k=1, force_tile="256x256")
+    assert i0["perm_block"] == 1 and i1["perm_block"] == 64
+    assert np.array_equal(c0, c1)
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 8, 8), (8, 16, 64), (24, 40, 16)])
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_tiny_shapes(M, N, K, la, lb):
+    _say("tiny", M, N, K, la, lb)
+    inp = _inputs_int(M, N, K, la, lb, "f16", seed=81)
+    c, _ = run_gpu(inp, "f16", "f32", split_k=1)
+    _, ref = reference(inp, "f16", "f32")
+    assert np.array_equal(c, ref)
