@@ -1,0 +1,286 @@
+"""Benchmark of the operand-layout GEMM on one MI355X.
+
+A step is one C = A*B of the 4096^3 fp16 GEMM in BLAS "NN" storage (A column-major, i.e.
+M-contiguous and transposed in registers by the loader; B column-major, K-contiguous),
+fp32 accumulate, fp16 output, inputs N(0,1)/sqrt(K), resident in HBM before timing.
+
+Prints one JSON line: the headline TFLOP/s, a roofline object for the GEMM kernel
+(algorithmic 2*M*N*K flops per launch over the average launch duration measured with
+HIP events on the launch stream), the CPU oracle's throughput on a bounded sample of
+the same product, and the other workloads (other layouts, the non-power-of-2 bf16
+GEMM, skinny split-K and int4 shapes in GB/s) under "workloads".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only-headline]
+       python bench.py --copy-probe   (plain device copy of known size, for scaling
+                                       rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 matrix peak
+PEAK_GBS = 8000.0         # MI355X HBM3E
+MALL_BYTES = 256 << 20    # Infinity Cache: HBM-bound timings rotate over more than 2x this
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_square_4096_nn.txt")
+KERNEL_SRC = os.path.join(ROOT, "dense_gemm_operand_amd", "csrc", "kernels.hpp")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
+    summary is missing or was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for ln in open(TRAFFIC_FILE):
+        if ":" in ln and not ln.startswith("#"):
+            k, v = ln.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Gemm:
+    """One planned GEMM with device operands (and rotation copies for HBM-bound shapes)."""
+
+    def __init__(self, w, layout_a=None, layout_b=None, rotate_bytes=0):
+        import torch
+        import dense_gemm_operand_amd as dg
+        from dense_gemm_operand_amd import synth
+        self.dg, self.torch, self.w = dg, torch, w
+        t0 = time.time()
+        inp = synth.make_inputs(w, layout_a=layout_a, layout_b=layout_b)
+        self.inp = inp
+        self.M, self.N, self.K = inp["M"], inp["N"], inp["K"]
+        self.la, self.lb = inp["layout_a"], inp["layout_b"]
+        dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(
+            np.int16 if x.dtype == np.uint16 else np.uint8)).cuda()
+        A, B = dev(inp["A"]), dev(inp["B"])
+        S = dev(inp["scales"]) if w.int4 else None
+        self.in_bytes = A.numel() * A.element_size() + B.numel() * B.element_size() + \
+            (S.numel() * S.element_size() if S is not None else 0)
+        reps = 1
+        if rotate_bytes:
+            reps = max(1, -(-rotate_bytes // self.in_bytes))
+        self.sets = [(A, B, S)] + [(A.clone(), B.clone(), S.clone() if S is not None else None)
+                                   for _ in range(reps - 1)]
+        self.plan = dg.gemm_plan(self.M, self.N, self.K, self.la, self.lb, w.dtype_ab,
+                                 "u4" if w.int4 else w.dtype_ab, w.dtype_c, w.split_k,
+                                 dg.int4_quant() if w.int4 else None)
+        self.info = dg.gemm_plan_query(self.plan)
+        ob = 4 if w.dtype_c == "f32" else 2
+        self.C = torch.empty(self.M * self.N * ob // 2, dtype=torch.int16, device="cuda")
+        nws = dg.gemm_workspace_size(self.plan)
+        self.ws = torch.zeros(max(nws, 16), dtype=torch.uint8, device="cuda") if nws else None
+        self.flops = 2.0 * self.M * self.N * self.K
+        self.bytes = self.in_bytes + self.M * self.N * ob   # algorithmic: each operand once
+        self.i = 0
+        log(f"{w.name} {self.la}/{self.lb}: inputs ready in {time.time() - t0:.1f}s, "
+            f"{len(self.sets)} set(s), plan tile={self.info['tile_m']}x{self.info['tile_n']} "
+            f"split_k={self.info['split_k']}")
+
+    def run(self):
+        A, B, S = self.sets[self.i % len(self.sets)]
+        self.i += 1
+        self.dg.gemm_run(self.plan, A, B, S, self.C, self.ws)
+
+    def time_events(self, n: int, warm: int = 10) -> float:
+        """Average launch duration in ms from HIP event pairs on the launch stream."""
+        torch = self.torch
+        for _ in range(warm):
+            self.run()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        torch.cuda.synchronize()
+        for s, e in ev:
+            s.record()
+            self.run()
+            e.record()
+        torch.cuda.synchronize()
+        d = sorted(s.elapsed_time(e) for s, e in ev)
+        return float(np.mean(d)), float(d[len(d) // 2]), float(d[0])
+
+    def close(self):
+        self.dg.gemm_plan_destroy(self.plan)
+
+
+def cpu_baseline(g: Gemm, budget_s: float = 12.0):
+    """The oracle (untuned, all host threads) on a bounded sample: whole rows of the same
+    product. Also returns the rows for a parity spot check of the GPU result."""
+    import oracle
+    inp, w = g.inp, g.w
+    t0 = time.time()
+    a = oracle.operand_a(inp["A"], g.M, g.K, g.la, w.dtype_ab)
+    b = oracle.operand_b(inp["B"], g.K, g.N, g.lb, "u4" if w.int4 else w.dtype_ab,
+                         inp.get("scales"))
+    prep = time.time() - t0
+    probe = min(g.M, 2 * oracle.threads())
+    t1 = time.time()
+    oracle.gemm_f64(a, b, (0, probe))
+    per_row = max((time.time() - t1) / probe, 1e-6)
+    rows = int(max(1, min(g.M, (budget_s - prep) / per_row)))
+    rng = np.random.default_rng(7)
+    r0 = int(rng.integers(0, g.M - rows + 1))
+    t2 = time.time()
+    c64 = oracle.gemm_f64(a, b, (r0, r0 + rows))
+    dt = time.time() - t2 + prep
+    flops = 2.0 * rows * g.N * g.K
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"rows {r0}..{r0 + rows - 1} of the {g.M}x{g.N}x{g.K} product "
+                      f"({flops / 1e9:.1f} GFLOP, fp64, operand decode included, {dt:.1f}s)"}, \
+        (r0, rows, c64)
+
+
+def spot_check(g: Gemm, r0: int, rows: int, c64: np.ndarray) -> dict:
+    import oracle
+    g.run()
+    g.torch.cuda.synchronize()
+    fmt = g.w.dtype_c
+    ob = 4 if fmt == "f32" else 2
+    raw = g.C.cpu().numpy().view(np.uint32 if ob == 4 else np.uint16).reshape(g.M, g.N)
+    got = oracle.decode(raw[r0:r0 + rows], fmt)
+    ref = oracle.decode(oracle.encode(c64, fmt), fmt)
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    return {"rows": rows, "rel_frobenius": rel, "ok": rel <= 1e-3}
+
+
+def copy_probe():
+    import torch
+    n = 256 << 20
+    src = torch.ones(n // 2, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build runs on a single MI355X and has no "
+              f"multi-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_probe:
+        copy_probe()
+        return
+    from dense_gemm_operand_amd import synth
+    torch.cuda.set_device(0)
+
+    w = synth.WORKLOADS["square_4096"]
+    g = Gemm(w, "col", "col")
+    for _ in range(args.warmup):
+        g.run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g.run()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    value = g.flops / (ms_step * 1e-3) / 1e12
+    avg_ms, med_ms, min_ms = g.time_events(max(args.steps, 50))
+    achieved = g.flops / (avg_ms * 1e-3) / 1e12
+    log(f"headline: wall {ms_step * 1e3:.1f} us/step, event avg {avg_ms * 1e3:.1f} us "
+        f"(median {med_ms * 1e3:.1f}, min {min_ms * 1e3:.1f}) -> {achieved:.1f} TFLOP/s")
+
+    out = {
+        "metric": "TFLOP/s and % of dense MFMA peak, 4096^3 NN fp16 GEMM; GB/s for split-K",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "fp16 GEMM 4096x4096x4096, BLAS NN (A M-contiguous, B "
+                               "K-contiguous), fp32 accumulate, fp16 out, N(0,1)/sqrt(K)",
+                   "M": 4096, "N": 4096, "K": 4096, "layout_a": "col", "layout_b": "col",
+                   "tile": f"{g.info['tile_m']}x{g.info['tile_n']}x{g.info['tile_k']}",
+                   "split_k": g.info["split_k"]},
+        "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2),
+    }
+    traffic = read_traffic()
+    out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+                       "traffic": traffic,
+                       "kernel_avg_us": round(avg_ms * 1e3, 2),
+                       "flops_per_launch": g.flops}
+    if not args.no_cpu:
+        cb, (r0, rows, c64) = cpu_baseline(g)
+        out["cpu_baseline"] = cb
+        out["parity_spot_check"] = spot_check(g, r0, rows, c64)
+    g.close()
+    del g
+    torch.cuda.empty_cache()
+
+    if not args.only_headline:
+        extra = []
+        cases = [
+            ("square_4096", "row", "row", "mfma"), ("square_4096", "col", "row", "mfma"),
+            ("square_4096", "row", "col", "mfma"), ("nonpow2_bf16", None, None, "mfma"),
+            ("square_tt_256", None, None, "mfma"), ("int4_m4096", None, None, "mfma"),
+            ("skinny_splitk", None, None, "hbm"), ("int4_m16", None, None, "hbm"),
+        ]
+        for name, la, lb, bound in cases:
+            wl = synth.WORKLOADS[name]
+            rot = 2 * MALL_BYTES + (64 << 20) if bound == "hbm" else 0
+            h = Gemm(wl, la, lb, rotate_bytes=rot)
+            avg, med, mn = h.time_events(100 if bound == "hbm" else 50)
+            rec = {"workload": name, "M": h.M, "N": h.N, "K": h.K, "layout_a": h.la,
+                   "layout_b": h.lb, "dtype": wl.dtype_ab + ("+u4" if wl.int4 else ""),
+                   "out": wl.dtype_c, "split_k": h.info["split_k"],
+                   "tile": f"{h.info['tile_m']}x{h.info['tile_n']}", "us_avg": round(avg * 1e3, 2),
+                   "us_median": round(med * 1e3, 2),
+                   "tflops": round(h.flops / (avg * 1e-3) / 1e12, 2),
+                   "gbs": round(h.bytes / (avg * 1e-3) / 1e9, 1),
+                   "input_sets": len(h.sets)}
+            rec["pct_peak"] = round(100 * (rec["tflops"] / PEAK_TFLOPS if bound == "mfma"
+                                           else rec["gbs"] / PEAK_GBS), 2)
+            rec["bound"] = bound
+            log(json.dumps(rec))
+            extra.append(rec)
+            h.close()
+            del h
+            torch.cuda.empty_cache()
+        out["workloads"] = extra
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

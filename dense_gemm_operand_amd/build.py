@@ -18,10 +18,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # -packed-fp32-ops: never form packed fp32 VALU ops; -ffp-contract=off: no FMA contraction
 # (the int4 dequant must round exactly once, in its binary16 multiply).
-COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
+COMMON = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument"]
-SOURCES = ["kernels.hip", "host.cpp"]
+SOURCES = ["inst_f16.hip", "inst_bf16.hip", "inst_misc.hip", "host.cpp"]
 
 
 def _compile(src: str) -> str:

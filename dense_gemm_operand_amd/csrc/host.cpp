@@ -70,8 +70,11 @@ int cu_count_for(int* device, int* status) {
 
 // Candidate matching the request, or -1.
 int find_variant(int kernel, const Plan& p, int tm, int tn, int perm) {
+  // DGEMM_FORCE_WAVES=<n> restricts tiled variants to n waves per workgroup (tuning).
+  const int waves = env_int("DGEMM_FORCE_WAVES", 0);
   for (int i = 0; i < variant_count(); ++i) {
     const VariantInfo& v = variant_info(i);
+    if (kernel == KERNEL_TILE && waves > 0 && v.waves != waves) continue;
     if (v.kernel != kernel || v.dtype_a != p.dtype_a || v.dtype_b != p.dtype_b) continue;
     if (kernel == KERNEL_TILE) {
       if (v.layout_a != p.layout_a || v.layout_b != p.layout_b) continue;

@@ -1,3 +1,4 @@
+#pragma once
 // HIP kernels for gfx950 (CDNA4): C = A * B with operands in any row/column-major
 // layout, fp16/bf16 (or int4 B) in, fp32 accumulate, fp32/fp16/bf16 out.
 //
@@ -11,7 +12,7 @@
 //      (v_perm_b32; Triton PR 5223, "Feature description"), giving eight K-contiguous
 //      16-byte vectors, one per M/N index.
 //   3. 128-bit LDS stores into padded, row-permuted, K-contiguous tiles (lds_layout.hpp).
-//   4. 128-bit LDS reads of matrix-core fragments, v_mfma_f32_16x16x32_{f16,bf16}.
+//   4. 128-bit LDS reads of matrix-core fragments, v_mfma_f32_32x32x16_{f16,bf16}.
 //      Two LDS stages: the global loads of step t+1 are in flight while step t's
 //      fragments are multiplied; one barrier per step.
 //   5. Split-K across workgroups (BitBLAS PR 268, "SplitK Infer"; the K origin of split
@@ -42,6 +43,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -83,14 +85,14 @@ __device__ __forceinline__ uint16_t ld16b(__amdgpu_buffer_rsrc_t r, uint32_t off
 // 2t in the low half of dword t). v_perm_b32 (D, S0, S1, sel): byte i of D is byte
 // sel.byte[i] of the 8-byte value S0:S1 (S1 = bytes 0..3). Selector 0x05040100 joins the
 // low halves of S1 and S0, 0x07060302 their high halves.
-__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      out[e][t] = __builtin_amdgcn_perm(in[2 * t + 1][e >> 1], in[2 * t][e >> 1], sel);
-  }
+// Output row e of a 4 x 8 block (four K rows of eight elements): its four K values as
+// two dwords (two byte permutes).
+__device__ __forceinline__ u32x2 transpose_row4(const u32x4 (&in)[4], int e) {
+  const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+  u32x2 r;
+  r[0] = __builtin_amdgcn_perm(in[1][e >> 1], in[0][e >> 1], sel);
+  r[1] = __builtin_amdgcn_perm(in[3][e >> 1], in[2][e >> 1], sel);
+  return r;
 }
 
 // Eight 4-bit codes of one dword (byte b: low nibble = code of K index 2b, high nibble =
@@ -148,14 +150,14 @@ struct KArgs {
 // the workgroup stores them (coalesced, thread-major) into split z's slot, the last
 // workgroup to arrive at the tile's counter sums all splits in ascending order and
 // returns true; the others return false. The counter is reset for the next run.
-template <int NV, int THREADS>
-__device__ __forceinline__ bool splitk_fixup(f32x4 (&acc)[NV], const KArgs& a, int tile,
+template <class V, int NV, int THREADS>
+__device__ __forceinline__ bool splitk_fixup(V (&acc)[NV], const KArgs& a, int tile,
                                              int z, int sk, int tiles) {
   __shared__ int s_last;
   const int tid = threadIdx.x;
-  f32x4* base = reinterpret_cast<f32x4*>(a.part);
+  V* base = reinterpret_cast<V*>(a.part);
   const size_t per_tile = (size_t)NV * THREADS;
-  f32x4* mine = base + ((size_t)z * tiles + tile) * per_tile;
+  V* mine = base + ((size_t)z * tiles + tile) * per_tile;
 #pragma unroll
   for (int v = 0; v < NV; ++v) mine[(size_t)v * THREADS + tid] = acc[v];
   __syncthreads();
@@ -170,9 +172,9 @@ __device__ __forceinline__ bool splitk_fixup(f32x4 (&acc)[NV], const KArgs& a, i
   __threadfence();
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    f32x4 s = (z == 0) ? acc[v] : base[((size_t)0 * tiles + tile) * per_tile + (size_t)v * THREADS + tid];
+    V s = (z == 0) ? acc[v] : base[((size_t)0 * tiles + tile) * per_tile + (size_t)v * THREADS + tid];
     for (int b = 1; b < sk; ++b) {
-      const f32x4 p = (b == z) ? acc[v]
+      const V p = (b == z) ? acc[v]
                                : base[((size_t)b * tiles + tile) * per_tile + (size_t)v * THREADS + tid];
       s += p;
     }
@@ -185,38 +187,130 @@ __device__ __forceinline__ bool splitk_fixup(f32x4 (&acc)[NV], const KArgs& a, i
 
 // ================================================================= tiled kernel
 
+// One load slot of a thread: a block of VPB 16-byte vectors of one operand per K step.
+template <int VPB>
+struct Slot {
+  uint32_t off[VPB];  // byte offsets at the split's first K step (kOOB when outside)
+  int kofs;           // K index, relative to the step start, of the block's first element
+  int wbase;          // LDS byte offset of the block's first store (stage-relative)
+  int row;            // int4: N index of the block's row (scale lookup)
+};
+
+// How a thread moves its share of one operand tile (ROWS M or N indices x 64 K indices)
+// from HBM to LDS. KIND 0: K-contiguous storage. KIND 1: contiguous along M/N (the
+// operand is transposed in registers). KIND 2: int4 codes packed along K.
+//   KIND 0, block q, vector j: row j*ROWS/4 + q/8, 16-byte chunk q%8 of the step. Eight
+//     consecutive lanes cover one 128-byte row segment: whole lines in HBM, one LDS row.
+//   KIND 1, block q: kh = q%2, v = (q/2) % (ROWS/8), kg = (q/2) / (ROWS/8); vector j is K
+//     row 8kg + 4kh + j of elements 8v..8v+7 (thread rake: four consecutive K rows of one
+//     16-byte vector along M/N); consecutive lanes cover consecutive vectors of a K row.
+//     After the byte-permute transpose, element e's four K values (8 bytes) go to LDS
+//     row inv(8v + e) at byte 16kg + 8kh. The 16 lanes of one 64-bit store phase hold
+//     eight consecutive v and both kh: with the 64-row, stride-8 permutation they hit
+//     eight consecutive LDS rows (eight 16-byte bank groups) times two 8-byte halves.
+//   KIND 2, block q: row q/2, K half q%2 (32 codes, 16 bytes) -> four 16-byte stores of
+//     eight binary16 weights each.
+template <int KIND, int ROWS, int THREADS, RowPerm P>
+struct Operand {
+  static constexpr int BK = 64;
+  static constexpr int PITCH_B = 144;                // LDS row pitch: 128 B data + 16 B pad
+  static constexpr int VPB = KIND == 2 ? 1 : 4;
+  static constexpr int BLOCKS = ROWS * 2;            // blocks per K step
+  static constexpr int SLOTS = (BLOCKS + THREADS - 1) / THREADS;
+  static constexpr bool PARTIAL = BLOCKS % THREADS != 0;
+  // LDS-row step between the rows of one transposed vector: inv(8v + e) = inv(8v) + e*ES.
+  static constexpr int ES = P.block == 1 ? 1 : P.block / P.stride;
+  static constexpr bool es_ok() {
+    for (int v = 0; v < ROWS / 8; ++v)
+      for (int e = 0; e < 8; ++e)
+        if (P.inv(8 * v + e) != P.inv(8 * v) + e * ES) return false;
+    return true;
+  }
+  static_assert(es_ok(), "row permutation must step evenly inside a vector");
+  static_assert(ROWS % 64 == 0, "tile rows must be whole permutation blocks");
+
+  // Block q of this K split: offsets, K offset and LDS base. Blocks past BLOCKS (idle
+  // lanes of a partial slot) read nothing and store into their own dead row.
+  __device__ __forceinline__ static void setup(Slot<VPB>& s, int q, int row0, int rows_total,
+                                               int ld, int kb, int K) {
+    const bool live = q < BLOCKS;
+    if constexpr (KIND == 0) {
+      const int c = q % 8;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = j * (ROWS / 4) + q / 8;
+        s.off[j] = (live && row0 + r < rows_total) ? (uint32_t)((row0 + r) * ld + kb + 8 * c) * 2u : kOOB;
+      }
+      s.kofs = 8 * c;
+      s.wbase = P.inv(q / 8) * PITCH_B + 16 * c;
+    } else if constexpr (KIND == 1) {
+      const int kh = q % 2, v = (q / 2) % (ROWS / 8), kg = (q / 2) / (ROWS / 8);
+      const bool ok = live && row0 + 8 * v < rows_total;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        s.off[j] = ok ? (uint32_t)((kb + 8 * kg + 4 * kh + j) * ld + row0 + 8 * v) * 2u : kOOB;
+      s.kofs = 8 * kg + 4 * kh;
+      s.wbase = P.inv(8 * v) * PITCH_B + 16 * kg + 8 * kh;
+    } else {
+      const int r = q / 2, h = q % 2;
+      s.off[0] = (live && row0 + r < rows_total) ? (uint32_t)(row0 + r) * (uint32_t)(K / 2) + (uint32_t)((kb + 32 * h) / 2) : kOOB;
+      s.kofs = 32 * h;
+      s.wbase = P.inv(r) * PITCH_B + 64 * h;
+      s.row = row0 + r;
+    }
+    if (!live) s.wbase = ROWS * PITCH_B - 16;  // last pad bytes of the tile (never read)
+  }
+};
+
 template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN,
           bool PERM>
 struct TileCfg {
   static constexpr int BK = 64;
   static constexpr int THREADS = WM * WN * 64;
   static constexpr int WT_M = MT_M / WM, WT_N = MT_N / WN;
-  static constexpr int TM = WT_M / 16, TN = WT_N / 16;
+  static constexpr int TM = WT_M / 32, TN = WT_N / 32;   // 32x32 blocks per wave
   static constexpr int PITCH = 9;  // LDS row pitch in 16-byte units: 128 B data + 16 B pad
   static constexpr RowPerm PA = (!A_KC && PERM) ? RowPerm{64, 8} : RowPerm{1, 1};
   static constexpr RowPerm PB = (!B_KC && !U4B && PERM) ? RowPerm{64, 8} : RowPerm{1, 1};
+  using OpA = Operand<A_KC ? 0 : 1, MT_M, THREADS, PA>;
+  using OpB = Operand<U4B ? 2 : (B_KC ? 0 : 1), MT_N, THREADS, PB>;
   static constexpr int A16 = MT_M * PITCH, B16 = MT_N * PITCH;
   static constexpr int STAGE16 = A16 + B16;
   static constexpr int LDS_BYTES = 2 * STAGE16 * 16;
-  // Load units: eight 16-byte vectors each.
-  static constexpr int UA = MT_M * BK / 64;
-  static constexpr int UB = U4B ? MT_N * BK / 256 : MT_N * BK / 64;
-  static constexpr int NU = (UA + UB + THREADS - 1) / THREADS;
-  static_assert(WT_M % 16 == 0 && WT_N % 16 == 0, "wave tile must be whole 16x16 blocks");
-  static_assert(MT_M % 64 == 0 && MT_N % 64 == 0, "tile rows must be whole permutation blocks");
+  static_assert(WT_M % 32 == 0 && WT_N % 32 == 0, "wave tile must be whole 32x32 blocks");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
+
+template <class T>
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c);
+template <>
+__device__ __forceinline__ f32x16 mfma32x32x16<F16T>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mfma32x32x16<BF16T>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <int N> using IC = std::integral_constant<int, N>;
 
 template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN,
           bool PERM>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   using Cfg = TileCfg<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, PERM>;
+  using OpA = typename Cfg::OpA;
+  using OpB = typename Cfg::OpB;
   constexpr int BK = Cfg::BK, THREADS = Cfg::THREADS, PITCH = Cfg::PITCH;
-  constexpr int TM = Cfg::TM, TN = Cfg::TN, NU = Cfg::NU, UA = Cfg::UA, UB = Cfg::UB;
+  constexpr int TM = Cfg::TM, TN = Cfg::TN;
+  constexpr int SA = OpA::SLOTS, SB = OpB::SLOTS;
   constexpr RowPerm PA = Cfg::PA, PB = Cfg::PB;
   __shared__ __attribute__((aligned(16))) u32x4 lds[Cfg::LDS_BYTES / 16];
+  char* const ldsb = reinterpret_cast<char*>(lds);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wm = wave / WN, wn = wave % WN;
 
   // ---- tile index: XCD-aware remap (consecutive workgroup ids go round-robin over the
@@ -237,172 +331,180 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   const int kb = z * a.k_chunk;
   const int ke = min(a.K, kb + a.k_chunk);
   const int nt = ke > kb ? (ke - kb + BK - 1) / BK : 0;
+  const int klen = ke - kb;
 
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.A, a.bytesA);
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.B, a.bytesB);
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.S, a.bytesS);
 
-  u32x4 raw[NU][8];
-  uint16_t sraw[NU][8];
+  Slot<OpA::VPB> sa[SA];
+  Slot<OpB::VPB> sb[SB];
+#pragma unroll
+  for (int i = 0; i < SA; ++i) OpA::setup(sa[i], i * THREADS + tid, m0, a.M, a.ldA, kb, a.K);
+#pragma unroll
+  for (int i = 0; i < SB; ++i) OpB::setup(sb[i], i * THREADS + tid, n0, a.N, a.ldB, kb, a.K);
+  // Byte step of the offsets per K step.
+  const uint32_t dA = A_KC ? BK * 2u : (uint32_t)(BK * a.ldA) * 2u;
+  const uint32_t dB = U4B ? BK / 2u : (B_KC ? BK * 2u : (uint32_t)(BK * a.ldB) * 2u);
 
-  // Issue the global loads of K step `step` into raw/sraw.
-  auto load_step = [&](int step) {
-    const int k0 = kb + step * BK;
+  // Two register sets: set (j % 2) holds the global data of K step j between its loads
+  // (issued two steps ahead) and its LDS stores (one step ahead).
+  u32x4 ra[2][SA][OpA::VPB];
+  u32x4 rb[2][SB][OpB::VPB];
+  uint16_t rs[2][SB];
+
+  // Loads of K step `step` into set SET: vectors [J0, J1) of every block.
+  auto load_part = [&](auto SET_, int step, auto J0_, auto J1_) {
+    constexpr int SET = decltype(SET_)::value, J0 = decltype(J0_)::value, J1 = decltype(J1_)::value;
+    const int lim = klen - step * BK;  // K indices left in the split from this step on
 #pragma unroll
-    for (int i = 0; i < NU; ++i) {
-      const int u = i * THREADS + tid;
-      if (u < UA) {
-        if constexpr (A_KC) {
-          // unit u: vector j -> row j*MT_M/8 + u/8, 16-byte chunk u%8 of the K step
-          const int c = u % 8;
+    for (int i = 0; i < SA; ++i) {
+      const uint32_t d = dA * (uint32_t)step;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int r = j * (MT_M / 8) + u / 8;
-            const int gm = m0 + r, gk = k0 + 8 * c;
-            const bool ok = gm < a.M && gk < ke;
-            raw[i][j] = ld128(rA, ok ? (uint32_t)(gm * a.ldA + gk) * 2u : kOOB);
-          }
-        } else {
-          // unit u: vector v = u % (MT_M/8) along M, K rows 8*kg .. 8*kg+7
-          const int v = u % (MT_M / 8), kg = u / (MT_M / 8);
-          const int gm = m0 + 8 * v;
+      for (int j = J0; j < J1 && j < OpA::VPB; ++j) {
+        const bool ok = sa[i].kofs + (A_KC ? 0 : j) < lim;
+        ra[SET][i][j] = ld128(rA, ok ? sa[i].off[j] + d : kOOB);
+      }
+    }
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int gk = k0 + 8 * kg + j;
-            const bool ok = gm < a.M && gk < ke;
-            raw[i][j] = ld128(rA, ok ? (uint32_t)(gk * a.ldA + gm) * 2u : kOOB);
-          }
-        }
-      } else if (u < UA + UB) {
-        const int ub = u - UA;
+    for (int i = 0; i < SB; ++i) {
+      const uint32_t d = dB * (uint32_t)step;
+#pragma unroll
+      for (int j = J0; j < J1 && j < OpB::VPB; ++j) {
+        const bool ok = sb[i].kofs + ((B_KC || U4B) ? 0 : j) < lim;
+        rb[SET][i][j] = ld128(rB, ok ? sb[i].off[j] + d : kOOB);
         if constexpr (U4B) {
-          // vector j of unit ub -> x = j*UB + ub: row x/2 (N index), K half x%2 (32 codes)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int x = j * UB + ub;
-            const int gn = n0 + x / 2, gk = k0 + 32 * (x % 2);
-            const bool ok = gn < a.N && gk < ke;
-            raw[i][j] = ld128(rB, ok ? (uint32_t)gn * (uint32_t)(a.K / 2) + (uint32_t)(gk / 2) : kOOB);
-            sraw[i][j] = ld16b(rS, ok ? ((uint32_t)(gk / 128) * (uint32_t)a.N + gn) * 2u : kOOB);
-          }
-        } else if constexpr (B_KC) {
-          const int c = ub % 8;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int r = j * (MT_N / 8) + ub / 8;
-            const int gn = n0 + r, gk = k0 + 8 * c;
-            const bool ok = gn < a.N && gk < ke;
-            raw[i][j] = ld128(rB, ok ? (uint32_t)(gn * a.ldB + gk) * 2u : kOOB);
-          }
-        } else {
-          const int v = ub % (MT_N / 8), kg = ub / (MT_N / 8);
-          const int gn = n0 + 8 * v;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int gk = k0 + 8 * kg + j;
-            const bool ok = gn < a.N && gk < ke;
-            raw[i][j] = ld128(rB, ok ? (uint32_t)(gk * a.ldB + gn) * 2u : kOOB);
-          }
+          const int gk = kb + step * BK + sb[i].kofs;
+          rs[SET][i] = ld16b(rS, (ok && sb[i].row < a.N) ? ((uint32_t)(gk / 128) * (uint32_t)a.N + sb[i].row) * 2u : kOOB);
         }
       }
     }
   };
 
-  // Transpose / dequantise the loaded registers and store them into LDS stage `st`.
-  auto store_step = [&](int st) {
-    u32x4* sA = lds + st * Cfg::STAGE16;
-    u32x4* sB = sA + Cfg::A16;
+  // LDS stores of set SET into buffer BUF, part P of 4 (vector P of a K-contiguous
+  // block, transposed rows 2P and 2P+1, int4 chunk P).
+  auto store_part = [&](auto SET_, auto BUF_, auto P_) {
+    constexpr int SET = decltype(SET_)::value, BUF = decltype(BUF_)::value, P = decltype(P_)::value;
+    char* sA = ldsb + BUF * Cfg::STAGE16 * 16;
+    char* sB = sA + Cfg::A16 * 16;
 #pragma unroll
-    for (int i = 0; i < NU; ++i) {
-      const int u = i * THREADS + tid;
-      if (u < UA) {
-        if constexpr (A_KC) {
-          const int c = u % 8;
+    for (int i = 0; i < SA; ++i) {
+      if constexpr (A_KC) {
+        *reinterpret_cast<u32x4*>(sA + sa[i].wbase + P * (MT_M / 4) * 144) = ra[SET][i][P];
+      } else {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int r = j * (MT_M / 8) + u / 8;
-            sA[PA.inv(r) * PITCH + c] = raw[i][j];
-          }
-        } else {
-          const int v = u % (MT_M / 8), kg = u / (MT_M / 8);
-          u32x4 tr[8];
-          transpose8x8(raw[i], tr);
+        for (int e = 2 * P; e < 2 * P + 2; ++e)
+          *reinterpret_cast<u32x2*>(sA + sa[i].wbase + e * OpA::ES * 144) = transpose_row4(ra[SET][i], e);
+      }
+    }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sA[PA.inv(8 * v + e) * PITCH + kg] = tr[e];
-        }
-      } else if (u < UA + UB) {
-        const int ub = u - UA;
-        if constexpr (U4B) {
+    for (int i = 0; i < SB; ++i) {
+      if constexpr (U4B) {
+        const _Float16 s = __builtin_bit_cast(_Float16, rs[SET][i]);
+        const f16x2 s2 = {s, s};
+        *reinterpret_cast<u32x4*>(sB + sb[i].wbase + 16 * P) = dequant8(rb[SET][i][0][P], s2);
+      } else if constexpr (B_KC) {
+        *reinterpret_cast<u32x4*>(sB + sb[i].wbase + P * (MT_N / 4) * 144) = rb[SET][i][P];
+      } else {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int x = j * UB + ub;
-            const int r = x / 2, h = x % 2;
-            const _Float16 s = __builtin_bit_cast(_Float16, sraw[i][j]);
-            const f16x2 s2 = {s, s};
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              sB[PB.inv(r) * PITCH + 4 * h + q] = dequant8(raw[i][j][q], s2);
-          }
-        } else if constexpr (B_KC) {
-          const int c = ub % 8;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int r = j * (MT_N / 8) + ub / 8;
-            sB[PB.inv(r) * PITCH + c] = raw[i][j];
-          }
-        } else {
-          const int v = ub % (MT_N / 8), kg = ub / (MT_N / 8);
-          u32x4 tr[8];
-          transpose8x8(raw[i], tr);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sB[PB.inv(8 * v + e) * PITCH + kg] = tr[e];
-        }
+        for (int e = 2 * P; e < 2 * P + 2; ++e)
+          *reinterpret_cast<u32x2*>(sB + sb[i].wbase + e * OpB::ES * 144) = transpose_row4(rb[SET][i], e);
       }
     }
   };
 
-  f32x4 acc[TM * TN];
+  f32x16 acc[TM * TN];
 #pragma unroll
-  for (int i = 0; i < TM * TN; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < TM * TN; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
 
-  // Fragment reads: lane reads LDS row (16-row block base + lane%16), 16-byte chunk
-  // (lane/16) of the 32-K half step.
-  const int r16 = lane & 15, kc = lane >> 4;
-  const int a_rd = (wm * Cfg::WT_M + r16) * PITCH + kc;
-  const int b_rd = Cfg::A16 + (wn * Cfg::WT_N + r16) * PITCH + kc;
+  // Fragment reads (v_mfma_f32_32x32x16): lane reads LDS row (32-row block base +
+  // lane%32), 16-byte chunk 2*kk + lane/32 of the step's K sub-step kk.
+  const int r32 = lane & 31, kh = lane >> 5;
+  const int a_rd = (wm * Cfg::WT_M + r32) * PITCH + kh;
+  const int b_rd = Cfg::A16 + (wn * Cfg::WT_N + r32) * PITCH + kh;
 
-  if (nt > 0) {
-    load_step(0);
-    store_step(0);
-  }
-  __syncthreads();
-  for (int s = 0; s < nt; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < nt) load_step(s + 1);
-    const u32x4* st = lds + cur * Cfg::STAGE16;
+  // Instruction counts of one sub-step, for the interleaving below.
+  constexpr int N_MFMA = TM * TN;
+  constexpr int N_READ = TM + TN;
+  constexpr int N_WRITE = SA * (A_KC ? 1 : 2) + SB * (U4B ? 1 : (B_KC ? 1 : 2));
+  constexpr int N_VMEM = SA + SB * (U4B ? 2 : 1);
+
+  // K step s from LDS buffer CUR (= s % 2), four 16-K sub-steps kk. Sub-step kk also
+  // issues the fragment reads of sub-step kk+1, vector kk of every block of step s+2
+  // (into register set CUR, free since its data went to LDS last step) if LOAD, and part
+  // kk of the LDS stores of step s+1 (set CUR^1 -> buffer CUR^1, free since it was read
+  // last step) if STORE. The flags are compile-time so the loop body has no branches (a
+  // branch would make the compiler wait for every outstanding load at the join), and
+  // scheduling groups interleave the memory and permute work between the matrix-core
+  // instructions so it runs while they execute.
+  auto step = [&](int s, auto CUR_, auto LOAD_, auto STORE_) {
+    constexpr int CUR = decltype(CUR_)::value;
+    constexpr bool LOAD = decltype(LOAD_)::value, STORE = decltype(STORE_)::value;
+    const u32x4* st = lds + CUR * Cfg::STAGE16;
+    u32x4 fa[2][TM], fb[2][TN];
+    auto read = [&](auto KK_) {
+      constexpr int kk = decltype(KK_)::value;
 #pragma unroll
-    for (int h = 0; h < BK / 32; ++h) {
-      u32x4 fa[TM], fb[TN];
+      for (int i = 0; i < TM; ++i) fa[kk & 1][i] = st[a_rd + i * 32 * PITCH + 2 * kk];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = st[a_rd + i * 16 * PITCH + 4 * h];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = st[b_rd + j * 16 * PITCH + 4 * h];
+      for (int j = 0; j < TN; ++j) fb[kk & 1][j] = st[b_rd + j * 32 * PITCH + 2 * kk];
+    };
+    auto sub = [&](auto KK_) {
+      constexpr int kk = decltype(KK_)::value;
+      if constexpr (kk < 3) read(IC<kk + 1>{});
+      if constexpr (LOAD) load_part(CUR_, s + 2, IC<kk>{}, IC<kk + 1>{});
+      if constexpr (STORE) store_part(IC<CUR ^ 1>{}, IC<CUR ^ 1>{}, KK_);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i * TN + j] = mfma16x16x32<T>(fb[j], fa[i], acc[i * TN + j]);
-    }
-    if (s + 1 < nt) store_step(cur ^ 1);
+          acc[i * TN + j] = mfma32x32x16<T>(fb[kk & 1][j], fa[kk & 1][i], acc[i * TN + j]);
+      // one matrix-core instruction, then a share of the other work, repeated
+#pragma unroll
+      for (int g = 0; g < N_MFMA; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // MFMA
+        if (kk < 3 && g < N_READ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        if (STORE && g < N_WRITE) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+        if (LOAD && g < N_VMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);                          // VALU
+      }
+    };
+    static_assert(BK / 16 == 4, "four 16-K sub-steps per step");
+    read(IC<0>{});
+    sub(IC<0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    sub(IC<1>{});
+    __builtin_amdgcn_sched_barrier(0);
+    sub(IC<2>{});
+    __builtin_amdgcn_sched_barrier(0);
+    sub(IC<3>{});
     __syncthreads();
+  };
+
+  using TRUE = std::integral_constant<bool, true>;
+  // Every step loads two ahead and stores one ahead; loads past the split's end use
+  // out-of-range offsets and return zeros, so the loop runs an even number of steps (a
+  // padding step multiplies zeros and leaves the sums exact) and has no drain code.
+  load_part(IC<0>{}, 0, IC<0>{}, IC<4>{});
+  load_part(IC<1>{}, 1, IC<0>{}, IC<4>{});
+  store_part(IC<0>{}, IC<0>{}, IC<0>{});
+  store_part(IC<0>{}, IC<0>{}, IC<1>{});
+  store_part(IC<0>{}, IC<0>{}, IC<2>{});
+  store_part(IC<0>{}, IC<0>{}, IC<3>{});
+  __syncthreads();
+  for (int s = 0; s < nt; s += 2) {
+    step(s, IC<0>{}, TRUE{}, TRUE{});
+    step(s + 1, IC<1>{}, TRUE{}, TRUE{});
   }
 
   if (sk > 1) {
-    if (!splitk_fixup<TM * TN, THREADS>(acc, a, tile, z, sk, tiles)) return;
+    if (!splitk_fixup<f32x16, TM * TN, THREADS>(acc, a, tile, z, sk, tiles)) return;
   }
 
-  // ---- epilogue: acc (i, j) block: lane holds logical row fwd_A(LDS row of lane%16) and
-  // the four logical columns fwd_B(LDS rows 4*(lane/16) + 0..3).
+  // ---- epilogue: block (i, j), lane l holds logical row fwd_A(LDS row 32i + l%32) and,
+  // for g = 0..3, the four logical columns fwd_B(LDS rows 32j + 8g + 4(l/32) + 0..3).
   auto epilogue = [&](auto dt_tag) {
     constexpr int DT = decltype(dt_tag)::value;
     using O = typename OutT<DT>::type;
@@ -410,7 +512,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     constexpr int ROW_BYTES = MT_N * OB;
     constexpr int CP = ROW_BYTES + 16;                    // LDS pitch of the C tile
     constexpr int RPP0 = Cfg::LDS_BYTES / CP;
-    constexpr int RPP = RPP0 >= MT_M ? MT_M : (RPP0 / 16) * 16;  // rows per pass
+    constexpr int RPP = RPP0 >= MT_M ? MT_M : (RPP0 / 32) * 32;  // rows per pass
     constexpr int NPASS = (MT_M + RPP - 1) / RPP;
     constexpr int CPR = ROW_BYTES / 16;                   // 16-byte chunks per row
     char* cl = reinterpret_cast<char*>(lds);
@@ -420,22 +522,26 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
       const int lo = p * RPP;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const int m = PA.fwd(wm * Cfg::WT_M + i * 16 + r16);
+        const int m = PA.fwd(wm * Cfg::WT_M + i * 32 + r32);
         if (m < lo || m >= lo + RPP) continue;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const f32x4 v = acc[i * TN + j];
-          const int nb = wn * Cfg::WT_N + j * 16 + 4 * kc;
-          if constexpr (PB.block == 1) {
-            O* dst = reinterpret_cast<O*>(cl + (m - lo) * CP + nb * OB);
-            typedef O o4 __attribute__((ext_vector_type(4)));
-            o4 w = {cvt_out<DT>(v[0]), cvt_out<DT>(v[1]), cvt_out<DT>(v[2]), cvt_out<DT>(v[3])};
-            *reinterpret_cast<o4*>(dst) = w;
-          } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              O* dst = reinterpret_cast<O*>(cl + (m - lo) * CP + PB.fwd(nb + e) * OB);
-              *dst = cvt_out<DT>(v[e]);
+          for (int g = 0; g < 4; ++g) {
+            const int nb = wn * Cfg::WT_N + j * 32 + 8 * g + 4 * kh;
+            const f32x16& v = acc[i * TN + j];
+            if constexpr (PB.block == 1) {
+              O* dst = reinterpret_cast<O*>(cl + (m - lo) * CP + nb * OB);
+              typedef O o4 __attribute__((ext_vector_type(4)));
+              o4 w = {cvt_out<DT>(v[4 * g]), cvt_out<DT>(v[4 * g + 1]), cvt_out<DT>(v[4 * g + 2]),
+                      cvt_out<DT>(v[4 * g + 3])};
+              *reinterpret_cast<o4*>(dst) = w;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                O* dst = reinterpret_cast<O*>(cl + (m - lo) * CP + PB.fwd(nb + e) * OB);
+                *dst = cvt_out<DT>(v[4 * g + e]);
+              }
             }
           }
         }
@@ -578,7 +684,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
   }
 
   if (sk > 1) {
-    if (!splitk_fixup<NV, THREADS>(sum, a, tile, z, sk, gridDim.x)) return;
+    if (!splitk_fixup<f32x4, NV, THREADS>(sum, a, tile, z, sk, gridDim.x)) return;
   }
 
   // ---- store: position p = nb*64 + l holds row l%16, columns n0 + 16nb + 4(l/16) + 0..3
@@ -655,56 +761,10 @@ struct Variant {
                       16 * (NB), (U4) ? 128 : 64, W, W, 0, 0},                               \
           &launch_skinny<T, U4, NB, W, U>}
 
-static const Variant kVariants[] = {
-    // skinny split-K kernels (M <= 16)
-    SKINNY(F16T, false, 4, 4, 2),
-    SKINNY(BF16T, false, 4, 4, 2),
-    SKINNY(F16T, true, 4, 4, 2),
-    // tiled kernels, every layout pair
-    TILE_LAYOUTS(F16T, 256, 256, 2, 4),
-    TILE_LAYOUTS(BF16T, 256, 256, 2, 4),
-    TILE_LAYOUTS(F16T, 192, 320, 2, 4),
-    TILE_LAYOUTS(BF16T, 192, 320, 2, 4),
-    TILE_LAYOUTS(F16T, 128, 128, 2, 2),
-    TILE_LAYOUTS(BF16T, 128, 128, 2, 2),
-    // int4 B (column-major codes), A either layout
-    TILE(F16T, true, true, true, 256, 256, 2, 4, true),
-    TILE(F16T, false, true, true, 256, 256, 2, 4, true),
-    TILE(F16T, true, true, true, 128, 128, 2, 2, true),
-    TILE(F16T, false, true, true, 128, 128, 2, 2, true),
-    // identity LDS row order (for comparisons of bank conflicts)
-    TILE(F16T, false, true, false, 256, 256, 2, 4, false),
-    TILE(F16T, true, false, false, 256, 256, 2, 4, false),
-};
 
-int variant_count() { return (int)(sizeof(kVariants) / sizeof(kVariants[0])); }
-const VariantInfo& variant_info(int i) { return kVariants[i].info; }
-
-int launch(const Plan& p, const RunArgs& r, void* stream) {
-  KArgs a;
-  a.A = r.A;
-  a.B = r.B;
-  a.S = r.scales;
-  a.C = r.C;
-  a.counters = reinterpret_cast<int*>(r.ws);
-  a.part = r.ws ? reinterpret_cast<float*>(reinterpret_cast<char*>(r.ws) + kCounterBytes) : nullptr;
-  a.M = (int)p.M;
-  a.N = (int)p.N;
-  a.K = (int)p.K;
-  a.ldA = (int)(p.layout_a == 0 ? p.K : p.M);
-  a.ldB = (int)(p.layout_b == 0 ? p.N : p.K);
-  const int eb_b = p.dtype_b == DT_U4 ? 1 : 2;
-  a.bytesA = (uint32_t)(p.M * p.K * 2);
-  a.bytesB = (uint32_t)(p.dtype_b == DT_U4 ? p.N * p.K / 2 : p.N * p.K * eb_b);
-  a.bytesS = (uint32_t)(p.dtype_b == DT_U4 ? (p.K / 128) * p.N * 2 : 0);
-  a.k_chunk = (int)p.k_chunk;
-  a.tiles_m = (int)((p.M + p.tile_m - 1) / p.tile_m);
-  a.tiles_n = (int)((p.N + p.tile_n - 1) / p.tile_n);
-  a.dtype_c = p.dtype_c;
-  const int ob = p.dtype_c == DT_F32 ? 4 : 2;
-  a.c_vec = ((p.N * ob) % 16 == 0) ? 1 : 0;
-  if (p.kernel == KERNEL_SKINNY) a.c_vec = (p.N % 4 == 0) ? 1 : 0;  // 4-element stores
-  return (int)kVariants[p.variant].fn(p, a, reinterpret_cast<hipStream_t>(stream));
-}
+// Instantiation tables, one per translation unit.
+int variants_f16(const Variant** out);
+int variants_bf16(const Variant** out);
+int variants_misc(const Variant** out);
 
 }  // namespace dg
