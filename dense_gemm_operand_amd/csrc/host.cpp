@@ -81,6 +81,12 @@ int find_variant(int kernel, const Plan& p, int tm, int tn, int perm) {
       if (v.tile_m != tm || v.tile_n != tn || v.perm != perm) continue;
     } else {
       if (v.layout_a != p.layout_a || v.layout_b != p.layout_b) continue;
+      // DGEMM_FORCE_SKINNY=<n-blocks>x<waves>x<depth> picks one skinny variant (tuning).
+      int nb = 0, w = 0, d = 0;
+      if (const char* fs = std::getenv("DGEMM_FORCE_SKINNY")) {
+        std::sscanf(fs, "%dx%dx%d", &nb, &w, &d);
+        if (v.tile_n != 16 * nb || v.waves != w || v.depth != d) continue;
+      }
     }
     return i;
   }
@@ -140,6 +146,7 @@ int make_plan(Plan& p, int split_k_req) {
   p.perm_block = (v.kernel == KERNEL_TILE && v.perm && transposed) ? 64 : 1;
   p.perm_stride = p.perm_block > 1 ? 8 : 1;
   p.lds_bytes = v.lds_bytes;
+  p.slots_per_cu = v.slots_per_cu;
   if (v.kernel == KERNEL_SKINNY) {
     p.lds_pad = 0;
     p.lds_bytes = v.waves * (v.tile_n / 16) * 64 * 16;
@@ -152,7 +159,9 @@ int make_plan(Plan& p, int split_k_req) {
   int sk = split_k_req;
   const int forced_sk = env_int("DGEMM_FORCE_SPLIT_K", 0);
   if (forced_sk > 0) sk = forced_sk;
-  if (sk == 0) sk = splitk_search(tiles, p.K, k_step, p.cu_count);
+  // The search counts workgroup slots: CUs times the workgroups the variant keeps
+  // resident per CU (the skinny kernels are small enough for two).
+  if (sk == 0) sk = splitk_search(tiles, p.K, k_step, p.cu_count * v.slots_per_cu);
   if (sk > 1 && tiles > kMaxCounters) sk = 1;
   p.split_k = sk;
   // chunk: ceil(K / sk) rounded up to the per-iteration granule of the kernel
@@ -302,6 +311,7 @@ int gemm_plan_query(gemm_plan_t plan, gemm_plan_info_t* info) {
   info->workspace_bytes = p.workspace_bytes;
   info->lds_bytes = p.lds_bytes;
   info->cu_count = p.cu_count;
+  info->slots_per_cu = p.slots_per_cu;
   return GEMM_OK;
 }
 

@@ -146,39 +146,55 @@ struct KArgs {
   int c_vec;            // 1 if every C row starts 16-byte aligned
 };
 
-// Split-K fix-up shared by both kernels. Every thread owns NV f32x4 partial vectors;
-// the workgroup stores them (coalesced, thread-major) into split z's slot, the last
-// workgroup to arrive at the tile's counter sums all splits in ascending order and
-// returns true; the others return false. The counter is reset for the next run.
+// Split-K fix-up shared by both kernels. Every thread owns NV vectors of LEN fp32
+// partial sums; the workgroup stores them into split z's slot, the last workgroup to
+// arrive at the tile's counter adds all splits in ascending split order and returns
+// true; the others return false. The counter is reset for the next run.
+//
+// Cross-XCD visibility without cache maintenance: partials are written and read with
+// agent-scope relaxed atomics (device-coherent stores and loads that go to the memory
+// side, past the XCD-private L2), every thread waits for its stores to complete before
+// the workgroup barrier, and only then is the counter incremented (agent scope). An
+// agent-scope release/acquire fence would instead write back and invalidate the whole
+// L2 of the XCD for every workgroup. Layout: element-major [split][tile][v][e][thread],
+// so every store and load instruction covers consecutive addresses.
 template <class V, int NV, int THREADS>
 __device__ __forceinline__ bool splitk_fixup(V (&acc)[NV], const KArgs& a, int tile,
                                              int z, int sk, int tiles) {
+  constexpr int LEN = sizeof(V) / sizeof(float);
   __shared__ int s_last;
   const int tid = threadIdx.x;
-  V* base = reinterpret_cast<V*>(a.part);
-  const size_t per_tile = (size_t)NV * THREADS;
-  V* mine = base + ((size_t)z * tiles + tile) * per_tile;
+  const size_t per_tile = (size_t)NV * LEN * THREADS;
+  float* mine = a.part + ((size_t)z * tiles + tile) * per_tile;
 #pragma unroll
-  for (int v = 0; v < NV; ++v) mine[(size_t)v * THREADS + tid] = acc[v];
+  for (int v = 0; v < NV; ++v)
+#pragma unroll
+    for (int e = 0; e < LEN; ++e)
+      __hip_atomic_store(mine + ((size_t)v * LEN + e) * THREADS + tid, acc[v][e], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
   __syncthreads();
   if (tid == 0) {
-    __threadfence();
-    const int old = __hip_atomic_fetch_add(a.counters + tile, 1, __ATOMIC_ACQ_REL,
+    const int old = __hip_atomic_fetch_add(a.counters + tile, 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
     s_last = (old == sk - 1);
   }
   __syncthreads();
   if (!s_last) return false;
-  __threadfence();
+  const float* base = a.part + (size_t)tile * per_tile;
+  const size_t split_stride = (size_t)tiles * per_tile;
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    V s = (z == 0) ? acc[v] : base[((size_t)0 * tiles + tile) * per_tile + (size_t)v * THREADS + tid];
-    for (int b = 1; b < sk; ++b) {
-      const V p = (b == z) ? acc[v]
-                               : base[((size_t)b * tiles + tile) * per_tile + (size_t)v * THREADS + tid];
-      s += p;
+#pragma unroll
+    for (int e = 0; e < LEN; ++e) {
+      const size_t idx = ((size_t)v * LEN + e) * THREADS + tid;
+      float s = (z == 0) ? acc[v][e] : __hip_atomic_load(base + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int b = 1; b < sk; ++b)
+        s += (b == z) ? acc[v][e]
+                      : __hip_atomic_load(base + b * split_stride + idx, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+      acc[v][e] = s;
     }
-    acc[v] = s;
   }
   if (tid == 0)
     __hip_atomic_store(a.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -277,6 +293,9 @@ struct TileCfg {
   static constexpr int A16 = MT_M * PITCH, B16 = MT_N * PITCH;
   static constexpr int STAGE16 = A16 + B16;
   static constexpr int LDS_BYTES = 2 * STAGE16 * 16;
+  // Register sets for in-flight global data: two (loads two steps ahead) unless a thread
+  // owns more than four blocks, where the second set would not fit in the register file.
+  static constexpr int NSETS = (OpA::SLOTS + OpB::SLOTS) > 4 ? 1 : 2;
   static_assert(WT_M % 32 == 0 && WT_N % 32 == 0, "wave tile must be whole 32x32 blocks");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
@@ -347,11 +366,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   const uint32_t dA = A_KC ? BK * 2u : (uint32_t)(BK * a.ldA) * 2u;
   const uint32_t dB = U4B ? BK / 2u : (B_KC ? BK * 2u : (uint32_t)(BK * a.ldB) * 2u);
 
-  // Two register sets: set (j % 2) holds the global data of K step j between its loads
-  // (issued two steps ahead) and its LDS stores (one step ahead).
-  u32x4 ra[2][SA][OpA::VPB];
-  u32x4 rb[2][SB][OpB::VPB];
-  uint16_t rs[2][SB];
+  // Register sets: with two, set (j % 2) holds the global data of K step j between its
+  // loads (issued two steps ahead) and its LDS stores (one step ahead); with one, step j's
+  // data is loaded and stored during step j-1.
+  constexpr int NS = Cfg::NSETS;
+  u32x4 ra[NS][SA][OpA::VPB];
+  u32x4 rb[NS][SB][OpB::VPB];
+  uint16_t rs[NS][SB];
 
   // Loads of K step `step` into set SET: vectors [J0, J1) of every block.
   auto load_part = [&](auto SET_, int step, auto J0_, auto J1_) {
@@ -454,8 +475,18 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     auto sub = [&](auto KK_) {
       constexpr int kk = decltype(KK_)::value;
       if constexpr (kk < 3) read(IC<kk + 1>{});
-      if constexpr (LOAD) load_part(CUR_, s + 2, IC<kk>{}, IC<kk + 1>{});
-      if constexpr (STORE) store_part(IC<CUR ^ 1>{}, IC<CUR ^ 1>{}, KK_);
+      if constexpr (NS == 2) {
+        if constexpr (LOAD) load_part(CUR_, s + 2, IC<kk>{}, IC<kk + 1>{});
+        if constexpr (STORE) store_part(IC<CUR ^ 1>{}, IC<CUR ^ 1>{}, KK_);
+      } else {
+        if constexpr (LOAD && kk == 0) load_part(IC<0>{}, s + 1, IC<0>{}, IC<4>{});
+        if constexpr (STORE && kk >= 2) {
+          store_part(IC<0>{}, IC<CUR ^ 1>{}, IC<2 * (kk - 2)>{});
+          store_part(IC<0>{}, IC<CUR ^ 1>{}, IC<2 * (kk - 2) + 1>{});
+        }
+      }
+      constexpr int n_vmem = NS == 2 ? N_VMEM : (kk == 0 ? 4 * N_VMEM : 0);
+      constexpr int n_write = NS == 2 ? N_WRITE : (kk >= 2 ? 2 * N_WRITE : 0);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -466,8 +497,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
       for (int g = 0; g < N_MFMA; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // MFMA
         if (kk < 3 && g < N_READ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-        if (STORE && g < N_WRITE) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
-        if (LOAD && g < N_VMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // VMEM read
+        if (STORE && g < n_write) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+        if (LOAD && g < n_vmem) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // VMEM read
         __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);                          // VALU
       }
     };
@@ -488,7 +519,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   // out-of-range offsets and return zeros, so the loop runs an even number of steps (a
   // padding step multiplies zeros and leaves the sums exact) and has no drain code.
   load_part(IC<0>{}, 0, IC<0>{}, IC<4>{});
-  load_part(IC<1>{}, 1, IC<0>{}, IC<4>{});
+  if constexpr (NS == 2) load_part(IC<NS - 1>{}, 1, IC<0>{}, IC<4>{});
   store_part(IC<0>{}, IC<0>{}, IC<0>{});
   store_part(IC<0>{}, IC<0>{}, IC<1>{});
   store_part(IC<0>{}, IC<0>{}, IC<2>{});
@@ -747,7 +778,8 @@ struct Variant {
 #define TILE(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM)                                       \
   Variant{VariantInfo{KERNEL_TILE, dt_code<T>(), (U4) ? DT_U4 : dt_code<T>(), (AKC) ? 0 : 1,  \
                       (BKC) ? 1 : 0, MTM, MTN, 64, (WM) * (WN), 1, PERM,                     \
-                      TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM>::LDS_BYTES},          \
+                      TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM>::LDS_BYTES,           \
+                      TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM>::NSETS, 1},           \
           &launch_tile<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM>}
 
 #define TILE_LAYOUTS(T, MTM, MTN, WM, WN)                                                    \
@@ -756,9 +788,9 @@ struct Variant {
   TILE(T, false, true, false, MTM, MTN, WM, WN, true),                                     \
   TILE(T, false, false, false, MTM, MTN, WM, WN, true)
 
-#define SKINNY(T, U4, NB, W, U)                                                              \
+#define SKINNY(T, U4, NB, W, U, SLOTS)                                                       \
   Variant{VariantInfo{KERNEL_SKINNY, dt_code<T>(), (U4) ? DT_U4 : dt_code<T>(), 0, 1, 16,     \
-                      16 * (NB), (U4) ? 128 : 64, W, W, 0, 0},                               \
+                      16 * (NB), (U4) ? 128 : 64, W, W, 0, 0, U, SLOTS},                     \
           &launch_skinny<T, U4, NB, W, U>}
 
 

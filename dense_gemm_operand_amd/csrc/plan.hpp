@@ -27,6 +27,7 @@ struct Plan {
   int64_t workspace_bytes = 0;
   int32_t lds_bytes = 0;
   int32_t cu_count = 0;
+  int32_t slots_per_cu = 1;
   int32_t device = -1;
 };
 
@@ -53,6 +54,8 @@ struct VariantInfo {
   int32_t wave_split_k;
   int32_t perm;                   // 1 = permuted LDS rows for transposed operands
   int32_t lds_bytes;
+  int32_t depth;                  // skinny: K iterations in flight per wave
+  int32_t slots_per_cu;           // workgroups assumed resident per CU by the split-K search
 };
 
 int variant_count();

@@ -81,7 +81,8 @@ typedef struct {
   int64_t grid_x, grid_y, grid_z;
   int64_t workspace_bytes; /* what gemm_run needs (0 when split_k == 1) */
   int32_t lds_bytes;       /* LDS per workgroup */
-  int32_t cu_count;        /* compute units the split-K search assumed */
+  int32_t cu_count;        /* compute units of the device */
+  int32_t slots_per_cu;    /* resident workgroups per CU the split-K search assumed */
 } gemm_plan_info_t;
 
 /* Make a plan for C (M x N, row-major, dtype_c) = A (M x K) * B (K x N).
@@ -91,8 +92,9 @@ typedef struct {
  *   dtype_a == GEMM_F16, layout_b == GEMM_COL_MAJOR (codes packed along K) and a
  *   non-null `quant` (otherwise quant must be NULL or is ignored).
  * dtype_c: GEMM_F32, GEMM_F16 or GEMM_BF16 (round-to-nearest-even from fp32 sums).
- * split_k: 0 lets the planner choose (waste-ratio search over the CU count, BitBLAS
- *   PR 268 "SplitK Infer", capped at 16); otherwise 1, 2, 4, 8 or 16.
+ * split_k: 0 lets the planner choose (waste-ratio search over the workgroup slots,
+ *   i.e. CU count times resident workgroups per CU, BitBLAS PR 268 "SplitK Infer",
+ *   capped at 16); otherwise 1, 2, 4, 8 or 16.
  * Constraints: M, N, K >= 1; the contiguous extent of each operand is a multiple of 8
  *   elements (K for row-major A and column-major B, M for column-major A, N for
  *   row-major B); int4 needs K % 128 == 0. Violations give GEMM_ERR_UNSUPPORTED.

@@ -116,7 +116,8 @@ def test_split_k_choice_matches_the_page_search(fake_cus, M, N, K, la, lb, dt, d
     info = dg.gemm_plan_query(p)
     dg.gemm_plan_destroy(p)
     step = info["tile_k"] * (info["waves"] if info["kernel"] == 1 else 1)
-    want = oracle.splitk_factor(M, N, K, info["tile_m"], info["tile_n"], step, 256)
+    want = oracle.splitk_factor(M, N, K, info["tile_m"], info["tile_n"], step,
+                                256 * info["slots_per_cu"])
     assert info["split_k"] == want
     tiles = -(-M // info["tile_m"]) * -(-N // info["tile_n"])
     assert info["grid_x"] * info["grid_y"] * info["grid_z"] == tiles * want
