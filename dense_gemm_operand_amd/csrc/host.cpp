@@ -75,6 +75,13 @@ int find_variant(int kernel, const Plan& p, int tm, int tn, int perm) {
   for (int i = 0; i < variant_count(); ++i) {
     const VariantInfo& v = variant_info(i);
     if (kernel == KERNEL_TILE && waves > 0 && v.waves != waves) continue;
+    // DGEMM_FORCE_SCHED=<0|1> restricts tiled variants to one main-loop schedule (tuning).
+    const int sched = env_int("DGEMM_FORCE_SCHED", -1);
+    if (kernel == KERNEL_TILE && sched >= 0 && v.sched != sched) continue;
+    // DGEMM_FORCE_DTL=<0|1> restricts tiled variants to ones without / with direct-to-LDS
+    // loads of K-contiguous operands (tuning, tests).
+    const int dtl = env_int("DGEMM_FORCE_DTL", -1);
+    if (kernel == KERNEL_TILE && dtl >= 0 && (v.dtl != 0) != (dtl != 0)) continue;
     if (v.kernel != kernel || v.dtype_a != p.dtype_a || v.dtype_b != p.dtype_b) continue;
     if (kernel == KERNEL_TILE) {
       if (v.layout_a != p.layout_a || v.layout_b != p.layout_b) continue;
@@ -147,6 +154,8 @@ int make_plan(Plan& p, int split_k_req) {
   p.perm_stride = p.perm_block > 1 ? 8 : 1;
   p.lds_bytes = v.lds_bytes;
   p.slots_per_cu = v.slots_per_cu;
+  p.direct_lds = v.kernel == KERNEL_TILE ? v.dtl : 0;
+  if (p.direct_lds == 3) p.lds_pad = 0;  // neither operand is stored by the threads
   if (v.kernel == KERNEL_SKINNY) {
     p.lds_pad = 0;
     p.lds_bytes = v.waves * (v.tile_n / 16) * 64 * 16;
@@ -312,6 +321,7 @@ int gemm_plan_query(gemm_plan_t plan, gemm_plan_info_t* info) {
   info->lds_bytes = p.lds_bytes;
   info->cu_count = p.cu_count;
   info->slots_per_cu = p.slots_per_cu;
+  info->direct_lds = p.direct_lds;
   return GEMM_OK;
 }
 

@@ -4,10 +4,15 @@
 namespace dg {
 
 static const Variant kTable[] = {
+    // Defaults first (the planner takes the first match): direct-to-LDS loads when an
+    // operand is K-contiguous, the ping-pong schedule when both are transposed.
+    TILE_LAYOUTS_DTL(F16T, 256, 256, 2, 4),
+    TILE_LAYOUTS_PP(F16T, 256, 256, 2, 4),
     TILE_LAYOUTS(F16T, 256, 256, 2, 4),
     TILE_LAYOUTS(F16T, 256, 256, 2, 2),
     TILE_LAYOUTS(F16T, 192, 320, 2, 2),
     TILE_LAYOUTS(F16T, 128, 128, 2, 2),
+    TILE_LAYOUTS_DTL(F16T, 256, 256, 2, 2),
 };
 
 int variants_f16(const Variant** out) {

@@ -278,24 +278,99 @@ struct Operand {
   }
 };
 
+// A K-contiguous operand moved by direct global->LDS loads (buffer_load ... lds): the
+// data never passes through registers and no LDS store instruction is issued, so the
+// wave keeps issuing matrix-core instructions while the tile streams in. LDS rows are
+// 128 bytes (64 K values) without padding; the 16-byte chunk c of row r is kept in slot
+// c ^ swz(r), swz(r) = (r >> 1) & 7 (a chunk permutation of the K-contiguous layout), so
+// that a fragment read (lanes on 32 consecutive rows, one chunk each) touches every bank
+// group once per 16 lanes. One load instruction of a wave fills eight whole LDS rows
+// (1 KiB): lane t writes row t/8, slot t%8, and therefore loads chunk (t%8) ^ swz(row) of
+// that row, so the eight lanes of a row still read one whole 128-byte line.
+__device__ __forceinline__ constexpr int dtl_swz(int r) { return (r >> 1) & 7; }
+
+// Buffer resource words (base, stride 0, num_records, gfx9-family data format) for
+// instructions written as inline assembly.
+__device__ __forceinline__ u32x4 rsrc_words(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p);
+}
+
+template <int ROWS, int THREADS>
+struct DtlOperand {
+  static constexpr int WAVES = THREADS / 64;
+  static constexpr int NI = ROWS / (8 * WAVES);  // load instructions per wave and K step
+  static_assert(ROWS % (8 * WAVES) == 0, "every wave fills whole groups of eight rows");
+  uint32_t off[NI];  // byte offsets at the split's first K step (kOOB outside the operand)
+  int kofs[NI];      // K index of the lane's chunk relative to the step start
+
+  __device__ __forceinline__ void setup(int lane, int wave, int row0, int rows_total, int ld,
+                                        int kb) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int r = 8 * (wave * NI + j) + lane / 8;
+      const int c = (lane & 7) ^ dtl_swz(r);
+      off[j] = row0 + r < rows_total ? (uint32_t)((row0 + r) * ld + 8 * c) * 2u + (uint32_t)kb * 2u : kOOB;
+      kofs[j] = 8 * c;
+    }
+  }
+  // Loads of one K step (byte step d from the split's first step; lim = K indices left)
+  // into the operand's LDS region at byte address `base` of one stage. Written as inline
+  // assembly so that the compiler, which cannot tell the LDS regions apart, does not make
+  // every later LDS access wait for these loads; the kernel waits for them itself (a full
+  // s_waitcnt before the barrier that ends the step). The wait states cover a scalar
+  // register written by a vector instruction just before (the resource and M0 value) and
+  // the M0 write before an LDS-bound load.
+  __device__ __forceinline__ void issue(const u32x4& rs, uint32_t base, int wave, uint32_t d,
+                                        int lim) const {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const uint32_t o = kofs[j] < lim ? off[j] + d : kOOB;
+      const uint32_t m0v = base + (uint32_t)(wave * NI + j) * 1024u;
+      asm volatile(
+          "s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+          :
+          : "v"(o), "s"(m0v), "s"(rs)
+          : "memory", "m0");
+    }
+  }
+};
+
 template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN,
-          bool PERM>
+          bool PERM, bool DTL>
 struct TileCfg {
   static constexpr int BK = 64;
   static constexpr int THREADS = WM * WN * 64;
   static constexpr int WT_M = MT_M / WM, WT_N = MT_N / WN;
   static constexpr int TM = WT_M / 32, TN = WT_N / 32;   // 32x32 blocks per wave
-  static constexpr int PITCH = 9;  // LDS row pitch in 16-byte units: 128 B data + 16 B pad
   static constexpr RowPerm PA = (!A_KC && PERM) ? RowPerm{64, 8} : RowPerm{1, 1};
   static constexpr RowPerm PB = (!B_KC && !U4B && PERM) ? RowPerm{64, 8} : RowPerm{1, 1};
+  // Direct-to-LDS loads for K-contiguous operands (not for int4 codes, which are
+  // dequantised in registers).
+  static constexpr bool A_DTL = DTL && A_KC;
+  static constexpr bool B_DTL = DTL && B_KC && !U4B;
+  static constexpr bool ANY_DTL = A_DTL || B_DTL;
   using OpA = Operand<A_KC ? 0 : 1, MT_M, THREADS, PA>;
   using OpB = Operand<U4B ? 2 : (B_KC ? 0 : 1), MT_N, THREADS, PB>;
-  static constexpr int A16 = MT_M * PITCH, B16 = MT_N * PITCH;
+  using DA = DtlOperand<MT_M, THREADS>;
+  using DB = DtlOperand<MT_N, THREADS>;
+  // Register-staged load slots per thread (none for a direct-to-LDS operand).
+  static constexpr int SA = A_DTL ? 0 : OpA::SLOTS, SB = B_DTL ? 0 : OpB::SLOTS;
+  // LDS row pitch in 16-byte units: 128 B of data, plus 16 B of padding for operands
+  // stored by the threads (none for direct-to-LDS rows, which use the chunk swizzle).
+  static constexpr int PA16 = A_DTL ? 8 : 9, PB16 = B_DTL ? 8 : 9;
+  static constexpr int A16 = MT_M * PA16, B16 = MT_N * PB16;
   static constexpr int STAGE16 = A16 + B16;
   static constexpr int LDS_BYTES = 2 * STAGE16 * 16;
   // Register sets for in-flight global data: two (loads two steps ahead) unless a thread
   // owns more than four blocks, where the second set would not fit in the register file.
-  static constexpr int NSETS = (OpA::SLOTS + OpB::SLOTS) > 4 ? 1 : 2;
+  static constexpr int NSETS = (SA + SB) > 4 ? 1 : 2;
+  static_assert(!ANY_DTL || NSETS == 2, "direct-to-LDS schedule keeps loads a step ahead");
   static_assert(WT_M % 32 == 0 && WT_N % 32 == 0, "wave tile must be whole 32x32 blocks");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
@@ -316,14 +391,17 @@ __device__ __forceinline__ f32x16 mfma32x32x16<BF16T>(u32x4 a, u32x4 b, f32x16 c
 template <int N> using IC = std::integral_constant<int, N>;
 
 template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN,
-          bool PERM>
+          bool PERM, bool PP, bool DTL>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
-  using Cfg = TileCfg<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, PERM>;
+  using Cfg = TileCfg<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, PERM, DTL>;
   using OpA = typename Cfg::OpA;
   using OpB = typename Cfg::OpB;
-  constexpr int BK = Cfg::BK, THREADS = Cfg::THREADS, PITCH = Cfg::PITCH;
+  constexpr int BK = Cfg::BK, THREADS = Cfg::THREADS;
+  constexpr int PA16 = Cfg::PA16, PB16 = Cfg::PB16;
   constexpr int TM = Cfg::TM, TN = Cfg::TN;
-  constexpr int SA = OpA::SLOTS, SB = OpB::SLOTS;
+  constexpr int SA = Cfg::SA, SB = Cfg::SB;
+  constexpr int SA1 = SA > 0 ? SA : 1, SB1 = SB > 0 ? SB : 1;  // array extents
+  static_assert(!(PP && Cfg::ANY_DTL), "the ping-pong schedule stores every operand itself");
   constexpr RowPerm PA = Cfg::PA, PB = Cfg::PB;
   __shared__ __attribute__((aligned(16))) u32x4 lds[Cfg::LDS_BYTES / 16];
   char* const ldsb = reinterpret_cast<char*>(lds);
@@ -356,8 +434,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.B, a.bytesB);
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.S, a.bytesS);
 
-  Slot<OpA::VPB> sa[SA];
-  Slot<OpB::VPB> sb[SB];
+  Slot<OpA::VPB> sa[SA1];
+  Slot<OpB::VPB> sb[SB1];
+  typename Cfg::DA da;
+  typename Cfg::DB db;
+  if constexpr (Cfg::A_DTL) da.setup(lane, wave, m0, a.M, a.ldA, kb);
+  if constexpr (Cfg::B_DTL) db.setup(lane, wave, n0, a.N, a.ldB, kb);
 #pragma unroll
   for (int i = 0; i < SA; ++i) OpA::setup(sa[i], i * THREADS + tid, m0, a.M, a.ldA, kb, a.K);
 #pragma unroll
@@ -370,9 +452,20 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   // loads (issued two steps ahead) and its LDS stores (one step ahead); with one, step j's
   // data is loaded and stored during step j-1.
   constexpr int NS = Cfg::NSETS;
-  u32x4 ra[NS][SA][OpA::VPB];
-  u32x4 rb[NS][SB][OpB::VPB];
-  uint16_t rs[NS][SB];
+  u32x4 ra[NS][SA1][OpA::VPB];
+  u32x4 rb[NS][SB1][OpB::VPB];
+  uint16_t rs[NS][SB1];
+
+  // Direct-to-LDS loads of K step `step` into LDS buffer BUF.
+  const u32x4 wA = rsrc_words(a.A, a.bytesA), wB = rsrc_words(a.B, a.bytesB);
+  const uint32_t lds0 = lds_addr(ldsb);
+  auto dtl = [&](int step, auto BUF_) {
+    constexpr int BUF = decltype(BUF_)::value;
+    const uint32_t sA = lds0 + BUF * Cfg::STAGE16 * 16;
+    const int lim = klen - step * BK;
+    if constexpr (Cfg::A_DTL) da.issue(wA, sA, wave, dA * (uint32_t)step, lim);
+    if constexpr (Cfg::B_DTL) db.issue(wB, sA + Cfg::A16 * 16, wave, dB * (uint32_t)step, lim);
+  };
 
   // Loads of K step `step` into set SET: vectors [J0, J1) of every block.
   auto load_part = [&](auto SET_, int step, auto J0_, auto J1_) {
@@ -442,9 +535,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
 
   // Fragment reads (v_mfma_f32_32x32x16): lane reads LDS row (32-row block base +
   // lane%32), 16-byte chunk 2*kk + lane/32 of the step's K sub-step kk.
+  // Per 16-K sub-step kk, in 16-byte units (stage-relative); block i adds 32 rows.
   const int r32 = lane & 31, kh = lane >> 5;
-  const int a_rd = (wm * Cfg::WT_M + r32) * PITCH + kh;
-  const int b_rd = Cfg::A16 + (wn * Cfg::WT_N + r32) * PITCH + kh;
+  int a_rd[4], b_rd[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int ca = Cfg::A_DTL ? ((2 * kk + kh) ^ dtl_swz(r32)) : 2 * kk + kh;
+    const int cb = Cfg::B_DTL ? ((2 * kk + kh) ^ dtl_swz(r32)) : 2 * kk + kh;
+    a_rd[kk] = (wm * Cfg::WT_M + r32) * PA16 + ca;
+    b_rd[kk] = Cfg::A16 + (wn * Cfg::WT_N + r32) * PB16 + cb;
+  }
 
   // Instruction counts of one sub-step, for the interleaving below.
   constexpr int N_MFMA = TM * TN;
@@ -468,9 +568,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     auto read = [&](auto KK_) {
       constexpr int kk = decltype(KK_)::value;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) fa[kk & 1][i] = st[a_rd + i * 32 * PITCH + 2 * kk];
+      for (int i = 0; i < TM; ++i) fa[kk & 1][i] = st[a_rd[kk] + i * 32 * PA16];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fb[kk & 1][j] = st[b_rd + j * 32 * PITCH + 2 * kk];
+      for (int j = 0; j < TN; ++j) fb[kk & 1][j] = st[b_rd[kk] + j * 32 * PB16];
     };
     auto sub = [&](auto KK_) {
       constexpr int kk = decltype(KK_)::value;
@@ -504,6 +604,15 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     };
     static_assert(BK / 16 == 4, "four 16-K sub-steps per step");
     read(IC<0>{});
+    if constexpr (Cfg::ANY_DTL) {
+      // Step s+1 straight into the other LDS buffer (its last reads were in step s-1,
+      // before the previous barrier), then the register loads of step s+2 (set CUR was
+      // stored during step s-1): both have the whole step to land before the wait that
+      // ends it.
+      dtl(s + 1, IC<CUR ^ 1>{});
+      load_part(CUR_, s + 2, IC<0>{}, IC<4>{});
+      __builtin_amdgcn_sched_barrier(0);
+    }
     sub(IC<0>{});
     __builtin_amdgcn_sched_barrier(0);
     sub(IC<1>{});
@@ -511,23 +620,117 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     sub(IC<2>{});
     __builtin_amdgcn_sched_barrier(0);
     sub(IC<3>{});
+    if constexpr (Cfg::ANY_DTL) __builtin_amdgcn_s_waitcnt(0);  // every load of the step
     __syncthreads();
   };
 
   using TRUE = std::integral_constant<bool, true>;
-  // Every step loads two ahead and stores one ahead; loads past the split's end use
-  // out-of-range offsets and return zeros, so the loop runs an even number of steps (a
-  // padding step multiplies zeros and leaves the sums exact) and has no drain code.
-  load_part(IC<0>{}, 0, IC<0>{}, IC<4>{});
-  if constexpr (NS == 2) load_part(IC<NS - 1>{}, 1, IC<0>{}, IC<4>{});
-  store_part(IC<0>{}, IC<0>{}, IC<0>{});
-  store_part(IC<0>{}, IC<0>{}, IC<1>{});
-  store_part(IC<0>{}, IC<0>{}, IC<2>{});
-  store_part(IC<0>{}, IC<0>{}, IC<3>{});
-  __syncthreads();
-  for (int s = 0; s < nt; s += 2) {
-    step(s, IC<0>{}, TRUE{}, TRUE{});
-    step(s + 1, IC<1>{}, TRUE{}, TRUE{});
+  if constexpr (!PP) {
+    // Every step loads two ahead and stores one ahead; loads past the split's end use
+    // out-of-range offsets and return zeros, so the loop runs an even number of steps (a
+    // padding step multiplies zeros and leaves the sums exact) and has no drain code.
+    if constexpr (Cfg::ANY_DTL) {
+      dtl(0, IC<0>{});
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    load_part(IC<0>{}, 0, IC<0>{}, IC<4>{});
+    if constexpr (NS == 2) load_part(IC<NS - 1>{}, 1, IC<0>{}, IC<4>{});
+    store_part(IC<0>{}, IC<0>{}, IC<0>{});
+    store_part(IC<0>{}, IC<0>{}, IC<1>{});
+    store_part(IC<0>{}, IC<0>{}, IC<2>{});
+    store_part(IC<0>{}, IC<0>{}, IC<3>{});
+    if constexpr (Cfg::ANY_DTL) __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    using LOADS = std::integral_constant<bool, !Cfg::ANY_DTL>;  // else issued at step start
+    for (int s = 0; s < nt; s += 2) {
+      step(s, IC<0>{}, LOADS{}, TRUE{});
+      step(s + 1, IC<1>{}, LOADS{}, TRUE{});
+    }
+  } else {
+    // Ping-pong schedule. The waves form two groups (wave rows wm = 0 and 1, one wave of
+    // each on every SIMD) that run the same program one phase apart, so in every phase
+    // one wave per SIMD issues matrix-core instructions on fragments already in
+    // registers while the other reads its next fragments from LDS and, once per step,
+    // transposes and stores the next step's tile and issues the global loads of the one
+    // after. Per step and wave: C(first half of K) | M(read second half; store step s+1;
+    // load step s+2) | C(second half) | M(read first half of step s+1), with a barrier
+    // after every phase. Group 1 starts one barrier late and group 0 ends with one extra
+    // barrier, so both execute the same number of barriers.
+    static_assert(WM == 2 && NS == 2, "ping-pong layout: two wave rows, one block per operand");
+    const int grp = wm;
+    u32x4 fa[2][TM], fb[2][TN];
+    auto readh = [&](int buf, auto H_) {
+      constexpr int H = decltype(H_)::value;
+      const u32x4* st = lds + buf * Cfg::STAGE16;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[q][i] = st[a_rd[2 * H + q] + i * 32 * PA16];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[q][j] = st[b_rd[2 * H + q] + j * 32 * PB16];
+      }
+    };
+    auto compute = [&]() {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i * TN + j] = mfma32x32x16<T>(fb[q][j], fa[q][i], acc[i * TN + j]);
+    };
+    // Barrier between phases, fenced so the scheduler cannot move matrix-core or memory
+    // instructions from one phase into another (MFMAs have no memory effects and would
+    // otherwise drift across a plain barrier).
+    auto phase_barrier = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto store_all = [&](int buf) {
+      if (buf == 0) {
+        store_part(IC<0>{}, IC<0>{}, IC<0>{});
+        store_part(IC<0>{}, IC<0>{}, IC<1>{});
+        store_part(IC<0>{}, IC<0>{}, IC<2>{});
+        store_part(IC<0>{}, IC<0>{}, IC<3>{});
+      } else {
+        store_part(IC<0>{}, IC<1>{}, IC<0>{});
+        store_part(IC<0>{}, IC<1>{}, IC<1>{});
+        store_part(IC<0>{}, IC<1>{}, IC<2>{});
+        store_part(IC<0>{}, IC<1>{}, IC<3>{});
+      }
+    };
+    load_part(IC<0>{}, 0, IC<0>{}, IC<4>{});
+    store_all(0);
+    load_part(IC<0>{}, 1, IC<0>{}, IC<4>{});
+    phase_barrier();
+    if (grp == 1) phase_barrier();
+    readh(0, IC<0>{});
+    phase_barrier();
+    for (int s = 0; s < nt; s += 2) {
+      // two steps per iteration so the buffer indices are compile-time
+      compute();
+      phase_barrier();
+      readh(0, IC<1>{});
+      store_all(1);
+      load_part(IC<0>{}, s + 2, IC<0>{}, IC<4>{});
+      phase_barrier();
+      compute();
+      phase_barrier();
+      readh(1, IC<0>{});
+      phase_barrier();
+      compute();
+      phase_barrier();
+      readh(1, IC<1>{});
+      store_all(0);
+      load_part(IC<0>{}, s + 3, IC<0>{}, IC<4>{});
+      phase_barrier();
+      compute();
+      phase_barrier();
+      readh(0, IC<0>{});
+      phase_barrier();
+    }
+    if (grp == 0) phase_barrier();
   }
 
   if (sk > 1) {
@@ -752,12 +955,13 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
 
 using LaunchFn = hipError_t (*)(const Plan&, const KArgs&, hipStream_t);
 
-template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN, bool PERM>
+template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN, bool PERM,
+          bool PP, bool DTL>
 hipError_t launch_tile(const Plan& p, const KArgs& a, hipStream_t s) {
-  using Cfg = TileCfg<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, PERM>;
+  using Cfg = TileCfg<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, PERM, DTL>;
   dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.grid_z);
-  hipLaunchKernelGGL((gemm_tile_kernel<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, PERM>), grid,
-                     dim3(Cfg::THREADS), 0, s, a);
+  hipLaunchKernelGGL((gemm_tile_kernel<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, PERM, PP, DTL>),
+                     grid, dim3(Cfg::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -775,12 +979,17 @@ struct Variant {
   LaunchFn fn;
 };
 
-#define TILE(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM)                                       \
+#define TILE_X(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, PP, DTL)                            \
   Variant{VariantInfo{KERNEL_TILE, dt_code<T>(), (U4) ? DT_U4 : dt_code<T>(), (AKC) ? 0 : 1,  \
                       (BKC) ? 1 : 0, MTM, MTN, 64, (WM) * (WN), 1, PERM,                     \
-                      TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM>::LDS_BYTES,           \
-                      TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM>::NSETS, 1},           \
-          &launch_tile<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM>}
+                      TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::LDS_BYTES,      \
+                      TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::NSETS, 1, PP,   \
+                      (TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::A_DTL ? 1 : 0) | \
+                      (TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::B_DTL ? 2 : 0)}, \
+          &launch_tile<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, PP, DTL>}
+#define TILE_PP(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, PP) TILE_X(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, PP, false)
+#define TILE(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM) TILE_X(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, false, false)
+#define TILE_DTL(T, AKC, BKC, U4, MTM, MTN, WM, WN) TILE_X(T, AKC, BKC, U4, MTM, MTN, WM, WN, true, false, true)
 
 #define TILE_LAYOUTS(T, MTM, MTN, WM, WN)                                                    \
   TILE(T, true, true, false, MTM, MTN, WM, WN, true),                                      \
@@ -788,9 +997,21 @@ struct Variant {
   TILE(T, false, true, false, MTM, MTN, WM, WN, true),                                     \
   TILE(T, false, false, false, MTM, MTN, WM, WN, true)
 
+// Layouts with at least one K-contiguous operand, direct-to-LDS loads for those.
+#define TILE_LAYOUTS_DTL(T, MTM, MTN, WM, WN)                                                \
+  TILE_DTL(T, true, true, false, MTM, MTN, WM, WN),                                        \
+  TILE_DTL(T, true, false, false, MTM, MTN, WM, WN),                                       \
+  TILE_DTL(T, false, true, false, MTM, MTN, WM, WN)
+
+#define TILE_LAYOUTS_PP(T, MTM, MTN, WM, WN)                                                 \
+  TILE_PP(T, true, true, false, MTM, MTN, WM, WN, true, true),                             \
+  TILE_PP(T, true, false, false, MTM, MTN, WM, WN, true, true),                            \
+  TILE_PP(T, false, true, false, MTM, MTN, WM, WN, true, true),                            \
+  TILE_PP(T, false, false, false, MTM, MTN, WM, WN, true, true)
+
 #define SKINNY(T, U4, NB, W, U, SLOTS)                                                       \
   Variant{VariantInfo{KERNEL_SKINNY, dt_code<T>(), (U4) ? DT_U4 : dt_code<T>(), 0, 1, 16,     \
-                      16 * (NB), (U4) ? 128 : 64, W, W, 0, 0, U, SLOTS},                     \
+                      16 * (NB), (U4) ? 128 : 64, W, W, 0, 0, U, SLOTS, 0, 0},               \
           &launch_skinny<T, U4, NB, W, U>}
 
 

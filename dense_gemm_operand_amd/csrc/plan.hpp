@@ -28,6 +28,7 @@ struct Plan {
   int32_t lds_bytes = 0;
   int32_t cu_count = 0;
   int32_t slots_per_cu = 1;
+  int32_t direct_lds = 0;              // bit 0: A, bit 1: B loaded straight into LDS
   int32_t device = -1;
 };
 
@@ -56,6 +57,8 @@ struct VariantInfo {
   int32_t lds_bytes;
   int32_t depth;                  // skinny: K iterations in flight per wave
   int32_t slots_per_cu;           // workgroups assumed resident per CU by the split-K search
+  int32_t sched;                  // tiled: 0 = software pipeline, 1 = ping-pong wave groups
+  int32_t dtl;                    // tiled: bit 0 A, bit 1 B loaded straight into LDS
 };
 
 int variant_count();

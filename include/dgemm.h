@@ -83,6 +83,10 @@ typedef struct {
   int32_t lds_bytes;       /* LDS per workgroup */
   int32_t cu_count;        /* compute units of the device */
   int32_t slots_per_cu;    /* resident workgroups per CU the split-K search assumed */
+  int32_t direct_lds;      /* bit 0 (A), bit 1 (B): the K-contiguous operand is loaded
+                              straight from global memory into LDS (rows of 128 B without
+                              padding, 16-byte chunks permuted by an XOR of the row);
+                              lds_pad_bytes then applies to the other operand only */
 } gemm_plan_info_t;
 
 /* Make a plan for C (M x N, row-major, dtype_c) = A (M x K) * B (K x N).

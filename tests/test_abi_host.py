@@ -133,6 +133,7 @@ def test_headline_plans(fake_cus):
     dg.gemm_plan_destroy(p)
     assert (i["tile_m"], i["tile_n"], i["split_k"], i["grid_x"]) == (256, 256, 1, 256)
     assert (i["perm_block"], i["perm_stride"], i["lds_pad_bytes"]) == (64, 8, 16)
+    assert i["direct_lds"] == 2   # B (column-major, K-contiguous) goes straight to LDS
     assert i["lds_bytes"] <= 160 * 1024
     p = dg.gemm_plan(3072, 5120, 6144, COL, ROW, BF16, BF16, BF16, 0)
     i = dg.gemm_plan_query(p)
@@ -182,3 +183,17 @@ def test_query_and_destroy_null():
     assert dg.lib().gemm_plan_query(None, None) == dg.GEMM_ERR_INVALID_ARG
     assert dg.lib().gemm_workspace_size(None, None) == dg.GEMM_ERR_INVALID_ARG
     dg.gemm_plan_destroy(None)
+
+
+@pytest.mark.parametrize("la,lb,bits", [(ROW, ROW, 1), (ROW, COL, 3), (COL, COL, 2)])
+def test_direct_to_lds_plans(fake_cus, la, lb, bits):
+    with env(DGEMM_FORCE_DTL=1):
+        p = dg.gemm_plan(4096, 4096, 4096, la, lb, F16, F16, F16, 0)
+        i = dg.gemm_plan_query(p)
+        dg.gemm_plan_destroy(p)
+    assert i["direct_lds"] == bits
+    assert i["lds_pad_bytes"] == (0 if bits == 3 else 16)
+    assert i["lds_bytes"] <= 160 * 1024
+    with env(DGEMM_FORCE_DTL=1):   # both operands transposed: nothing to load directly
+        with pytest.raises(dg.GemmError):
+            dg.gemm_plan(4096, 4096, 4096, COL, ROW, F16, F16, F16, 0)

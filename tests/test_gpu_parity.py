@@ -185,3 +185,66 @@ def test_tiny_shapes(M, N, K, la, lb):
     c, _ = run_gpu(inp, "f16", "f32", split_k=1)
     _, ref = reference(inp, "f16", "f32")
     assert np.array_equal(c, ref)
+
+
+DTL_LAYOUTS = [("row", "row"), ("row", "col"), ("col", "col")]   # a K-contiguous operand
+
+
+def _dtl_bits(la, lb):
+    return (1 if la == "row" else 0) | (2 if lb == "col" else 0)
+
+
+@pytest.mark.parametrize("waves", [8, 4])
+@pytest.mark.parametrize("la,lb", DTL_LAYOUTS)
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_direct_to_lds_integer_bit_exact(waves, la, lb, fmt):
+    # K-contiguous operands loaded straight into swizzled LDS rows; ragged M, N and K
+    # (K = 200: the last step has one 8-wide chunk) exercise the out-of-range zero fill
+    M, N, K = 392 + 8, 648, 200
+    _say("dtl-int", waves, la, lb, fmt)
+    inp = _inputs_int(M, N, K, la, lb, fmt, seed=91)
+    from helpers import env
+    with env(DGEMM_FORCE_DTL=1, DGEMM_FORCE_WAVES=waves):
+        c, info = run_gpu(inp, fmt, "f32", split_k=1, force_tile="256x256", guard=64)
+    assert info["direct_lds"] == _dtl_bits(la, lb) and info["waves"] == waves
+    _, ref = reference(inp, fmt, "f32")
+    assert np.array_equal(c, ref)
+
+
+@pytest.mark.parametrize("la,lb", DTL_LAYOUTS)
+def test_direct_to_lds_split_k_and_random(la, lb):
+    from helpers import env
+    M, N, K = 264, 520, 1032
+    _say("dtl-split", la, lb)
+    inp = _inputs_int(M, N, K, la, lb, "f16", seed=93)
+    _, ref = reference(inp, "f16", "f32")
+    with env(DGEMM_FORCE_DTL=1):
+        for sk in (1, 4):
+            c, info = run_gpu(inp, "f16", "f32", split_k=sk, force_tile="256x256", guard=16)
+            assert info["direct_lds"] == _dtl_bits(la, lb) and info["split_k"] == sk
+            assert np.array_equal(c, ref), sk
+        inp = _inputs_rand(520, 392, 328, la, lb, "bf16", seed=95)
+        c, _ = run_gpu(inp, "bf16", "bf16", split_k=1, force_tile="256x256", guard=16)
+    _, ref = reference(inp, "bf16", "bf16")
+    amax, bmax = operand_max(inp, "bf16")
+    check_tolerance(c, ref, "bf16", 328, amax, bmax, "dtl")
+
+
+# Every selectable 256x256 main-loop variant: (schedule, direct-to-LDS, waves).
+SCHED_VARIANTS = [(0, 0, 8), (0, 0, 4), (1, 0, 8), (0, 1, 8), (0, 1, 4)]
+
+
+@pytest.mark.parametrize("sched,dtl,waves", SCHED_VARIANTS)
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_every_schedule_variant_bit_exact(sched, dtl, waves, la, lb):
+    if dtl and (la, lb) == ("col", "row"):
+        pytest.skip("no K-contiguous operand to load directly")
+    from helpers import env
+    M, N, K = 264, 520, 456
+    _say("sched", sched, dtl, waves, la, lb)
+    inp = _inputs_int(M, N, K, la, lb, "f16", seed=97)
+    with env(DGEMM_FORCE_SCHED=sched, DGEMM_FORCE_DTL=dtl, DGEMM_FORCE_WAVES=waves):
+        c, info = run_gpu(inp, "f16", "f32", split_k=1, force_tile="256x256", guard=16)
+    assert info["waves"] == waves and (info["direct_lds"] != 0) == bool(dtl)
+    _, ref = reference(inp, "f16", "f32")
+    assert np.array_equal(c, ref)
