@@ -120,7 +120,9 @@ int make_plan(Plan& p, int split_k_req) {
     if (p.M <= 16 && !std::getenv("DGEMM_FORCE_TILE")) vi = find_variant(KERNEL_SKINNY, p, 0, 0, 0);
     if (vi < 0) {
       // Tiled kernel: among the instantiated tiles, the one with the least work per CU,
-      // i.e. ceil(tiles / CUs) * tile area (larger tiles first on ties).
+      // i.e. ceil(tiles / CUs) * tile area (larger tiles first on ties). A 4-wave tile is
+      // charged 5/4 of its area: measured per tile area it runs about that much slower than
+      // the 8-wave 256x256 kernels (one wave per SIMD hides less latency).
       static const int kTiles[][2] = {{256, 256}, {192, 320}, {128, 128}};
       // DGEMM_FORCE_TILE=<m>x<n> restricts the choice to one tile (tests, tuning).
       int force_m = 0, force_n = 0;
@@ -131,7 +133,7 @@ int make_plan(Plan& p, int split_k_req) {
         const int v = find_variant(KERNEL_TILE, p, t[0], t[1], no_perm ? 0 : 1);
         if (v < 0) continue;
         const int64_t tiles = cdiv(p.M, t[0]) * cdiv(p.N, t[1]);
-        const int64_t cost = cdiv(tiles, p.cu_count) * t[0] * t[1];
+        const int64_t cost = cdiv(tiles, p.cu_count) * t[0] * t[1] * (variant_info(v).waves >= 8 ? 4 : 5);
         if (best < 0 || cost < best) {
           best = cost;
           vi = v;

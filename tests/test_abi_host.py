@@ -135,10 +135,17 @@ def test_headline_plans(fake_cus):
     assert (i["perm_block"], i["perm_stride"], i["lds_pad_bytes"]) == (64, 8, 16)
     assert i["direct_lds"] == 2   # B (column-major, K-contiguous) goes straight to LDS
     assert i["lds_bytes"] <= 160 * 1024
+    # 3072x5120: the 8-wave 256x256 kernel (240 tiles) is charged less than the 4-wave
+    # 192x320 one (256 tiles); at 2880x5440 (264 tiles of 256x256, two rounds on 256 CUs,
+    # against 255 of 192x320) the non-power-of-2 tile wins
     p = dg.gemm_plan(3072, 5120, 6144, COL, ROW, BF16, BF16, BF16, 0)
     i = dg.gemm_plan_query(p)
     dg.gemm_plan_destroy(p)
-    assert (i["tile_m"], i["tile_n"], i["grid_x"]) == (192, 320, 256)   # non-power-of-2 tile
+    assert (i["tile_m"], i["tile_n"], i["grid_x"], i["waves"]) == (256, 256, 240, 8)
+    p = dg.gemm_plan(2880, 5440, 6144, COL, ROW, BF16, BF16, BF16, 0)
+    i = dg.gemm_plan_query(p)
+    dg.gemm_plan_destroy(p)
+    assert (i["tile_m"], i["tile_n"], i["grid_x"]) == (192, 320, 255)   # non-power-of-2 tile
 
 
 def test_lds_row_permutation_matches_the_page_formula():
