@@ -19,6 +19,9 @@ static const Variant kTable[] = {
     SKINNY(F16T, true, 4, 8, 4, 1),
     SKINNY(F16T, true, 2, 8, 4, 1),
     SKINNY(F16T, true, 8, 8, 2, 1),
+    SKINNY(F16T, true, 2, 16, 4, 1),
+    SKINNY(F16T, true, 2, 16, 2, 1),
+    SKINNY(F16T, true, 4, 8, 2, 2),
     // int4 B (column-major codes), A either layout
     TILE(F16T, true, true, true, 256, 256, 2, 4, true),
     TILE(F16T, false, true, true, 256, 256, 2, 4, true),

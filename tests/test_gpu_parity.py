@@ -248,3 +248,28 @@ def test_every_schedule_variant_bit_exact(sched, dtl, waves, la, lb):
     assert info["waves"] == waves and (info["direct_lds"] != 0) == bool(dtl)
     _, ref = reference(inp, "f16", "f32")
     assert np.array_equal(c, ref)
+
+
+INT4_SKINNY = ["4x16x2", "4x8x4", "2x8x4", "8x8x2", "2x16x4", "2x16x2", "4x8x2"]
+
+
+@pytest.mark.parametrize("v", INT4_SKINNY)
+@pytest.mark.parametrize("sk", [1, 4])
+def test_int4_skinny_variants_bit_exact(v, sk):
+    # integer activations and power-of-two scales: every weight (q - 8) * s and every
+    # partial sum is exact in fp32, so each variant must reproduce the oracle bit for bit;
+    # M = 5 and N = 200 leave ragged rows and columns in every tile width
+    from helpers import env
+    M, N, K = 5, 200, 2048
+    _say("int4-skinny", v, sk)
+    inp = _int4_inputs(M, N, K, seed=65)
+    rng = np.random.default_rng(66)
+    inp["A"] = synth.store(synth.integer_matrix(rng, M, K, -2, 2, "f16"), "row")
+    e = rng.integers(2, 7, size=(K // 128) * N)
+    inp["scales"] = synth.to_bits(np.ldexp(1.0, -e), "f16").reshape(-1)
+    with env(DGEMM_FORCE_SKINNY=v):
+        c, info = run_gpu(inp, "f16", "f32", split_k=sk, int4=True, guard=8)
+    assert info["kernel"] == 1 and info["split_k"] == sk
+    assert (info["tile_n"], info["waves"]) == (16 * int(v.split("x")[0]), int(v.split("x")[1]))
+    _, ref = reference(inp, "f16", "f32", int4=True)
+    assert np.array_equal(c, ref)
