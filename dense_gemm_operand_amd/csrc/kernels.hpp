@@ -782,6 +782,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
 
   // ---- epilogue: block (i, j), lane l holds logical row fwd_A(LDS row 32i + l%32) and,
   // for g = 0..3, the four logical columns fwd_B(LDS rows 32j + 8g + 4(l/32) + 0..3).
+  // The C tile is staged in LDS by A's LDS row (consecutive lanes on consecutive rows, so
+  // the stores spread over the banks) and each staged row goes to global row fwd_A(row).
   auto epilogue = [&](auto dt_tag) {
     constexpr int DT = decltype(dt_tag)::value;
     using O = typename OutT<DT>::type;
@@ -799,7 +801,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
       const int lo = p * RPP;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const int m = PA.fwd(wm * Cfg::WT_M + i * 32 + r32);
+        const int m = wm * Cfg::WT_M + i * 32 + r32;   // LDS row of A
         if (m < lo || m >= lo + RPP) continue;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -827,7 +829,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
       const int rows = min(RPP, MT_M - lo);  // the last pass may be short
       for (int c = tid; c < rows * CPR; c += THREADS) {
         const int row = c / CPR, cc = c % CPR;
-        const int gm = m0 + lo + row;
+        const int gm = m0 + PA.fwd(lo + row);
         const int gn = n0 + cc * (16 / OB);
         if (gm >= a.M || gn >= a.N) continue;
         const char* src = cl + row * CP + cc * 16;
