@@ -433,6 +433,18 @@ __device__ __forceinline__ f32x16 mfma32x32x16<BF16T>(u32x4 a, u32x4 b, f32x16 c
 
 template <int N> using IC = std::integral_constant<int, N>;
 
+// The epilogue's vector stores for a permuted B: within every wave's 32-row blocks, LDS rows
+// I + 8g (I = 32j + 4h + e, g = 0..3) map to four consecutive logical columns.
+template <RowPerm P, int WT_N>
+constexpr bool epilogue_cols_ok() {
+  if (P.block == 1) return true;
+  for (int base = 0; base < 4 * WT_N; base += 32)
+    for (int o = 0; o < 8; ++o)
+      for (int g = 1; g < 4; ++g)
+        if (P.fwd(base + o + 8 * g) != P.fwd(base + o) + g) return false;
+  return true;
+}
+
 template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN,
           bool PERM, bool PP, bool DTL>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
@@ -784,6 +796,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   // for g = 0..3, the four logical columns fwd_B(LDS rows 32j + 8g + 4(l/32) + 0..3).
   // The C tile is staged in LDS by A's LDS row (consecutive lanes on consecutive rows, so
   // the stores spread over the banks) and each staged row goes to global row fwd_A(row).
+  static_assert(epilogue_cols_ok<PB, Cfg::WT_N>(), "permuted B rows must give runs of four columns");
   auto epilogue = [&](auto dt_tag) {
     constexpr int DT = decltype(dt_tag)::value;
     using O = typename OutT<DT>::type;
@@ -815,11 +828,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
               o4 w = {cvt_out<DT>(v[4 * g]), cvt_out<DT>(v[4 * g + 1]), cvt_out<DT>(v[4 * g + 2]),
                       cvt_out<DT>(v[4 * g + 3])};
               *reinterpret_cast<o4*>(dst) = w;
-            } else {
+            } else if (g == 0) {
+              // B's rows are permuted: LDS rows nb + e + 8g (g = 0..3) hold the four
+              // consecutive logical columns fwd_B(nb + e) + g, so each e is one vector store.
+              typedef O o4 __attribute__((ext_vector_type(4)));
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 O* dst = reinterpret_cast<O*>(cl + (m - lo) * CP + PB.fwd(nb + e) * OB);
-                *dst = cvt_out<DT>(v[4 * g + e]);
+                o4 w = {cvt_out<DT>(v[e]), cvt_out<DT>(v[4 + e]), cvt_out<DT>(v[8 + e]),
+                        cvt_out<DT>(v[12 + e])};
+                *reinterpret_cast<o4*>(dst) = w;
               }
             }
           }
