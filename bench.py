@@ -13,6 +13,8 @@ GEMM, skinny split-K and int4 shapes in GB/s) under "workloads".
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only-headline]
        python bench.py --copy-probe   (plain device copy of known size, for scaling
                                        rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
+       python bench.py --workload NAME [--layout-a row|col --layout-b row|col] [--steps K]
+                      (only that workload, K launches: the target of per-workload profiles)
 """
 from __future__ import annotations
 
@@ -194,6 +196,51 @@ def spot_check(g: Gemm, r0: int, rows: int, c64: np.ndarray) -> dict:
     return {"rows": rows, "rel_frobenius": rel, "ok": rel <= 1e-3}
 
 
+def stream_context() -> dict:
+    """Device bandwidth context on the same box: a read-only pass (sum of a 2 GiB fp16
+    tensor, far beyond the 256 MiB Infinity Cache) and a 1 GiB device copy (read + write)."""
+    import torch
+    x = torch.ones(1 << 30, dtype=torch.float16, device="cuda")
+    y = torch.empty(1 << 29, dtype=torch.float16, device="cuda")
+    z = torch.empty_like(y)
+    for _ in range(2):
+        x.sum()
+        z.copy_(y)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    e[0].record()
+    for _ in range(5):
+        x.sum()
+    e[1].record()
+    for _ in range(5):
+        z.copy_(y)
+    e[2].record()
+    torch.cuda.synchronize()
+    rd = x.numel() * 2 * 5 / (e[0].elapsed_time(e[1]) * 1e-3) / 1e9
+    cp = 2 * y.numel() * 2 * 5 / (e[1].elapsed_time(e[2]) * 1e-3) / 1e9
+    del x, y, z
+    torch.cuda.empty_cache()
+    return {"stream_read_gbs": round(rd, 1), "copy_read_plus_write_gbs": round(cp, 1),
+            "note": "torch sum over 2 GiB fp16 and copy of 1 GiB, events over 5 runs each"}
+
+
+def run_workload(name: str, la, lb, steps: int):
+    """Only one workload, `steps` launches (rotating input sets for HBM-bound shapes)."""
+    import torch
+    from dense_gemm_operand_amd import synth
+    wl = synth.WORKLOADS[name]
+    hbm = name in ("skinny_splitk", "int4_m16")
+    g = Gemm(wl, la, lb, rotate_bytes=2 * MALL_BYTES + (64 << 20) if hbm else 0)
+    for _ in range(steps):
+        g.run()
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": name, "layout_a": g.la, "layout_b": g.lb, "launches": steps,
+                      "tile": f"{g.info['tile_m']}x{g.info['tile_n']}", "waves": g.info["waves"],
+                      "split_k": g.info["split_k"], "direct_lds": g.info["direct_lds"],
+                      "perm_block": g.info["perm_block"]}), flush=True)
+    g.close()
+
+
 def copy_probe():
     import torch
     n = 256 << 20
@@ -213,6 +260,9 @@ def main():
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--layout-a", default=None)
+    ap.add_argument("--layout-b", default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build runs on a single MI355X and has no "
@@ -221,6 +271,9 @@ def main():
     import torch
     if args.copy_probe:
         copy_probe()
+        return
+    if args.workload:
+        run_workload(args.workload, args.layout_a, args.layout_b, args.steps)
         return
     from dense_gemm_operand_amd import synth
     torch.cuda.set_device(0)
@@ -308,6 +361,7 @@ def main():
             del h
             torch.cuda.empty_cache()
         out["workloads"] = extra
+        out["context"] = stream_context()
     print(json.dumps(out), flush=True)
 
 
