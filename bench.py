@@ -331,16 +331,26 @@ def main():
 
     if not args.only_headline:
         extra = []
+        # (workload, layouts, bound, planner hooks): the last entries time the other loader
+        # for transposed operands (kept in global order in LDS, transposed by the LDS reads)
+        tr = {"DGEMM_FORCE_DTL": "2"}
         cases = [
-            ("square_4096", "row", "row", "mfma"), ("square_4096", "col", "row", "mfma"),
-            ("square_4096", "row", "col", "mfma"), ("nonpow2_bf16", None, None, "mfma"),
-            ("square_tt_256", None, None, "mfma"), ("int4_m4096", None, None, "mfma"),
-            ("skinny_splitk", None, None, "hbm"), ("int4_m16", None, None, "hbm"),
+            ("square_4096", "row", "row", "mfma", {}), ("square_4096", "col", "row", "mfma", {}),
+            ("square_4096", "row", "col", "mfma", {}), ("nonpow2_bf16", None, None, "mfma", {}),
+            ("square_tt_256", None, None, "mfma", {}), ("int4_m4096", None, None, "mfma", {}),
+            ("skinny_splitk", None, None, "hbm", {}), ("int4_m16", None, None, "hbm", {}),
+            ("square_4096", "col", "col", "mfma", tr), ("square_4096", "row", "row", "mfma", tr),
+            ("square_4096", "col", "row", "mfma", tr), ("nonpow2_bf16", None, None, "mfma", tr),
         ]
-        for name, la, lb, bound in cases:
+        for name, la, lb, bound, hooks in cases:
             wl = synth.WORKLOADS[name]
             rot = 2 * MALL_BYTES + (64 << 20) if bound == "hbm" else 0
-            h = Gemm(wl, la, lb, rotate_bytes=rot)
+            os.environ.update(hooks)
+            try:
+                h = Gemm(wl, la, lb, rotate_bytes=rot)
+            finally:
+                for k in hooks:
+                    os.environ.pop(k, None)
             avg, med, mn = h.time_events(100 if bound == "hbm" else 50)
             if avg < 0.1:   # short kernel: per-launch events would time the host enqueue gap
                 avg = med = mn = h.time_graph()
@@ -351,7 +361,11 @@ def main():
                    "us_median": round(med * 1e3, 2),
                    "tflops": round(h.flops / (avg * 1e-3) / 1e12, 2),
                    "gbs": round(h.bytes / (avg * 1e-3) / 1e9, 1),
-                   "input_sets": len(h.sets)}
+                   "input_sets": len(h.sets),
+                   "loader": ("transposing LDS reads" if h.info["direct_lds"] & 12 else
+                              "in-register transpose" if (h.la == "col" or h.lb == "row") else
+                              "K-contiguous"),
+                   "direct_lds": h.info["direct_lds"], "waves": h.info["waves"]}
             rec["pct_peak"] = round(100 * (rec["tflops"] / PEAK_TFLOPS if bound == "mfma"
                                            else rec["gbs"] / PEAK_GBS), 2)
             rec["bound"] = bound

@@ -78,10 +78,12 @@ int find_variant(int kernel, const Plan& p, int tm, int tn, int perm) {
     // DGEMM_FORCE_SCHED=<0|1> restricts tiled variants to one main-loop schedule (tuning).
     const int sched = env_int("DGEMM_FORCE_SCHED", -1);
     if (kernel == KERNEL_TILE && sched >= 0 && v.sched != sched) continue;
-    // DGEMM_FORCE_DTL=<0|1> restricts tiled variants to ones without / with direct-to-LDS
-    // loads of K-contiguous operands (tuning, tests).
+    // DGEMM_FORCE_DTL=<0|1|2> restricts tiled variants to ones without direct-to-LDS loads,
+    // with them for K-contiguous operands only, or with them for transposed operands too
+    // (transposed by the LDS reads) (tuning, tests).
     const int dtl = env_int("DGEMM_FORCE_DTL", -1);
-    if (kernel == KERNEL_TILE && dtl >= 0 && (v.dtl != 0) != (dtl != 0)) continue;
+    const int have = (v.dtl & 12) ? 2 : (v.dtl ? 1 : 0);
+    if (kernel == KERNEL_TILE && dtl >= 0 && have != dtl) continue;
     if (v.kernel != kernel || v.dtype_a != p.dtype_a || v.dtype_b != p.dtype_b) continue;
     if (kernel == KERNEL_TILE) {
       if (v.layout_a != p.layout_a || v.layout_b != p.layout_b) continue;
@@ -158,6 +160,13 @@ int make_plan(Plan& p, int split_k_req) {
   p.slots_per_cu = v.slots_per_cu;
   p.direct_lds = v.kernel == KERNEL_TILE ? v.dtl : 0;
   if (p.direct_lds == 3) p.lds_pad = 0;  // neither operand is stored by the threads
+  if (p.direct_lds & 12) {
+    // transposed operands in global order: 64 bytes of padding per 1 KiB LDS block and the
+    // K-row permutation B = 8, S = 4
+    p.lds_pad = 64;
+    p.perm_block = 8;
+    p.perm_stride = 4;
+  }
   if (v.kernel == KERNEL_SKINNY) {
     p.lds_pad = 0;
     p.lds_bytes = v.waves * (v.tile_n / 16) * 64 * 16;

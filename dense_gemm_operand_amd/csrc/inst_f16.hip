@@ -13,6 +13,7 @@ static const Variant kTable[] = {
     TILE_LAYOUTS(F16T, 192, 320, 2, 2),
     TILE_LAYOUTS(F16T, 128, 128, 2, 2),
     TILE_LAYOUTS_DTL(F16T, 256, 256, 2, 2),
+    TILE_LAYOUTS_DTLTR(F16T, 256, 256, 2, 4),
 };
 
 int variants_f16(const Variant** out) {

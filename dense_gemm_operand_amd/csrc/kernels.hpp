@@ -384,30 +384,109 @@ struct DtlOperand {
   }
 };
 
+// An operand whose contiguous index is M or N (256 of them per tile), moved by direct
+// global->LDS loads and transposed on the read instead of in registers (rocm-libraries
+// PR 2487: direct-to-LDS with padding per LDS block and a permutation of the perpendicular
+// dimension). LDS keeps global order: each K row is 256 contiguous M (or N) values, 512 B.
+// One load instruction of a wave fills a 1 KiB block (two K rows; lane t: row t/32,
+// elements 8(t%32)..+7), followed by 64 bytes of padding. Within each group of eight K rows
+// the rows are placed with the page's permutation, B = 8, S = 4: LDS row L of the group
+// holds K row fwd(L) = 4(L%2) + L/2, so block j holds K rows j and j+4.
+// ds_read_b64_tr_b16 (gfx950) gives lane t of each 16-lane group element t%4 of the 8-byte
+// chunks addressed by lanes t/4 + 4e, e = 0..3. Reading, per 16-lane group, K rows
+// kb + 4r + s/4 (block s/4 of the group, half r) at M chunk s%4 (s = lane%16) gives lane t
+// M index t and the four K values kb + 4r .. kb + 4r + 3; two reads (r = 0, 1) make one
+// v_mfma_f32_32x32x16 fragment in natural K order. The four rows read by a half-wave lie
+// in four consecutive blocks, 1088 B apart, i.e. at bank offsets 0, 64, 128 and 192 B, so
+// the reads are free of bank conflicts.
+template <int ROWS, int THREADS>
+struct DtlTrOperand {
+  static_assert(ROWS == 256, "two 512-byte K rows per 1 KiB load");
+  static constexpr int WAVES = THREADS / 64;
+  static constexpr int BLOCKS = 32;               // 64 K rows per step, two per block
+  static constexpr int NI = BLOCKS / WAVES;       // load instructions per wave and K step
+  static constexpr int BLOCK_BYTES = 1024 + 64;   // data + padding
+  static constexpr int BYTES = BLOCKS * BLOCK_BYTES;
+  static constexpr RowPerm P = RowPerm{8, 4};
+  static_assert(BLOCKS % WAVES == 0, "whole blocks per wave");
+  uint32_t off[NI];  // byte offsets at the split's first K step (kOOB outside the operand)
+  int krow[NI];      // K row of the lane, relative to the step start
+
+  __device__ __forceinline__ void setup(int lane, int wave, int row0, int rows_total, int ld,
+                                        int kb) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int b = wave * NI + j;                        // block: group b/4, slot b%4
+      const int k = 8 * (b / 4) + P.fwd(2 * (b % 4) + lane / 32);
+      const int m = row0 + 8 * (lane % 32);
+      off[j] = m < rows_total ? (uint32_t)((kb + k) * ld + m) * 2u : kOOB;
+      krow[j] = k;
+    }
+  }
+  __device__ __forceinline__ void issue(const u32x4& rs, uint32_t base, int wave, uint32_t d,
+                                        int lim) const {
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const uint32_t o = krow[j] < lim ? off[j] + d : kOOB;
+      const uint32_t m0v = base + (uint32_t)(wave * NI + j) * BLOCK_BYTES;
+      asm volatile(
+          "s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+          :
+          : "v"(o), "s"(m0v), "s"(rs)
+          : "memory", "m0");
+    }
+  }
+  // Lane's byte offset (stage-relative) for sub-step 0, read 0, fragment block 0, of the
+  // wave's rows starting at wrow; sub-step kk adds 8 * BLOCK_BYTES * kk, read 1 adds 512,
+  // fragment block i (32 rows) adds 64 i.
+  __device__ __forceinline__ static int read_base(int lane, int wrow) {
+    const int G = lane / 16, s = lane % 16;
+    return (4 * (G / 2) + s / 4) * BLOCK_BYTES + (16 * (G % 2) + 4 * (s % 4)) * 2 + wrow * 2;
+  }
+};
+
+// One v_mfma_f32_32x32x16 fragment from a transposed LDS block: reads at p and p + 512.
+__device__ __forceinline__ u32x4 tr_fragment(const char* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)p);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(p + 512));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
 template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN,
-          bool PERM, bool DTL>
+          bool PERM, int DTL>
 struct TileCfg {
   static constexpr int BK = 64;
   static constexpr int THREADS = WM * WN * 64;
   static constexpr int WT_M = MT_M / WM, WT_N = MT_N / WN;
   static constexpr int TM = WT_M / 32, TN = WT_N / 32;   // 32x32 blocks per wave
-  static constexpr RowPerm PA = (!A_KC && PERM) ? RowPerm{64, 8} : RowPerm{1, 1};
-  static constexpr RowPerm PB = (!B_KC && !U4B && PERM) ? RowPerm{64, 8} : RowPerm{1, 1};
-  // Direct-to-LDS loads for K-contiguous operands (not for int4 codes, which are
-  // dequantised in registers).
-  static constexpr bool A_DTL = DTL && A_KC;
-  static constexpr bool B_DTL = DTL && B_KC && !U4B;
-  static constexpr bool ANY_DTL = A_DTL || B_DTL;
+  // Direct-to-LDS loads (DTL >= 1) for K-contiguous operands (not for int4 codes, which
+  // are dequantised in registers); with DTL == 2 also for the transposed operands, which
+  // are then transposed by the LDS reads instead of in registers.
+  static constexpr bool A_DTL = DTL >= 1 && A_KC;
+  static constexpr bool B_DTL = DTL >= 1 && B_KC && !U4B;
+  static constexpr bool A_TR = DTL == 2 && !A_KC;
+  static constexpr bool B_TR = DTL == 2 && !B_KC && !U4B;
+  static constexpr bool ANY_DTL = A_DTL || B_DTL || A_TR || B_TR;
+  static constexpr RowPerm PA = (!A_KC && PERM && !A_TR) ? RowPerm{64, 8} : RowPerm{1, 1};
+  static constexpr RowPerm PB = (!B_KC && !U4B && PERM && !B_TR) ? RowPerm{64, 8} : RowPerm{1, 1};
   using OpA = Operand<A_KC ? 0 : 1, MT_M, THREADS, PA>;
   using OpB = Operand<U4B ? 2 : (B_KC ? 0 : 1), MT_N, THREADS, PB>;
   using DA = DtlOperand<MT_M, THREADS>;
   using DB = DtlOperand<MT_N, THREADS>;
+  using TA = DtlTrOperand<A_TR ? MT_M : 256, THREADS>;
+  using TB = DtlTrOperand<B_TR ? MT_N : 256, THREADS>;
   // Register-staged load slots per thread (none for a direct-to-LDS operand).
-  static constexpr int SA = A_DTL ? 0 : OpA::SLOTS, SB = B_DTL ? 0 : OpB::SLOTS;
+  static constexpr int SA = (A_DTL || A_TR) ? 0 : OpA::SLOTS;
+  static constexpr int SB = (B_DTL || B_TR) ? 0 : OpB::SLOTS;
   // LDS row pitch in 16-byte units: 128 B of data, plus 16 B of padding for operands
   // stored by the threads (none for direct-to-LDS rows, which use the chunk swizzle).
   static constexpr int PA16 = A_DTL ? 8 : 9, PB16 = B_DTL ? 8 : 9;
-  static constexpr int A16 = MT_M * PA16, B16 = MT_N * PB16;
+  static constexpr int A16 = A_TR ? TA::BYTES / 16 : MT_M * PA16;
+  static constexpr int B16 = B_TR ? TB::BYTES / 16 : MT_N * PB16;
   static constexpr int STAGE16 = A16 + B16;
   static constexpr int LDS_BYTES = 2 * STAGE16 * 16;
   // Register sets for in-flight global data: two (loads two steps ahead) unless a thread
@@ -446,7 +525,7 @@ constexpr bool epilogue_cols_ok() {
 }
 
 template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN,
-          bool PERM, bool PP, bool DTL>
+          bool PERM, bool PP, int DTL>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   using Cfg = TileCfg<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, PERM, DTL>;
   using OpA = typename Cfg::OpA;
@@ -493,8 +572,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   Slot<OpB::VPB> sb[SB1];
   typename Cfg::DA da;
   typename Cfg::DB db;
+  typename Cfg::TA ta;
+  typename Cfg::TB tb;
   if constexpr (Cfg::A_DTL) da.setup(lane, wave, m0, a.M, a.ldA, kb);
   if constexpr (Cfg::B_DTL) db.setup(lane, wave, n0, a.N, a.ldB, kb);
+  if constexpr (Cfg::A_TR) ta.setup(lane, wave, m0, a.M, a.ldA, kb);
+  if constexpr (Cfg::B_TR) tb.setup(lane, wave, n0, a.N, a.ldB, kb);
 #pragma unroll
   for (int i = 0; i < SA; ++i) OpA::setup(sa[i], i * THREADS + tid, m0, a.M, a.ldA, kb, a.K);
 #pragma unroll
@@ -520,6 +603,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     const int lim = klen - step * BK;
     if constexpr (Cfg::A_DTL) da.issue(wA, sA, wave, dA * (uint32_t)step, lim);
     if constexpr (Cfg::B_DTL) db.issue(wB, sA + Cfg::A16 * 16, wave, dB * (uint32_t)step, lim);
+    if constexpr (Cfg::A_TR) ta.issue(wA, sA, wave, dA * (uint32_t)step, lim);
+    if constexpr (Cfg::B_TR) tb.issue(wB, sA + Cfg::A16 * 16, wave, dB * (uint32_t)step, lim);
   };
 
   // Loads of K step `step` into set SET: vectors [J0, J1) of every block.
@@ -600,6 +685,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     a_rd[kk] = (wm * Cfg::WT_M + r32) * PA16 + ca;
     b_rd[kk] = Cfg::A16 + (wn * Cfg::WT_N + r32) * PB16 + cb;
   }
+  // Transposed direct-to-LDS operands: byte offsets of the transposing reads.
+  const int a_tr = Cfg::TA::read_base(lane, wm * Cfg::WT_M);
+  const int b_tr = Cfg::A16 * 16 + Cfg::TB::read_base(lane, wn * Cfg::WT_N);
 
   // Instruction counts of one sub-step, for the interleaving below.
   constexpr int N_MFMA = TM * TN;
@@ -623,9 +711,21 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     auto read = [&](auto KK_) {
       constexpr int kk = decltype(KK_)::value;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) fa[kk & 1][i] = st[a_rd[kk] + i * 32 * PA16];
+      for (int i = 0; i < TM; ++i) {
+        if constexpr (Cfg::A_TR)
+          fa[kk & 1][i] = tr_fragment(reinterpret_cast<const char*>(st) + a_tr +
+                                      8 * Cfg::TA::BLOCK_BYTES * kk + 64 * i);
+        else
+          fa[kk & 1][i] = st[a_rd[kk] + i * 32 * PA16];
+      }
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fb[kk & 1][j] = st[b_rd[kk] + j * 32 * PB16];
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (Cfg::B_TR)
+          fb[kk & 1][j] = tr_fragment(reinterpret_cast<const char*>(st) + b_tr +
+                                      8 * Cfg::TB::BLOCK_BYTES * kk + 64 * j);
+        else
+          fb[kk & 1][j] = st[b_rd[kk] + j * 32 * PB16];
+      }
     };
     auto sub = [&](auto KK_) {
       constexpr int kk = decltype(KK_)::value;
@@ -1047,7 +1147,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
 using LaunchFn = hipError_t (*)(const Plan&, const KArgs&, hipStream_t);
 
 template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN, bool PERM,
-          bool PP, bool DTL>
+          bool PP, int DTL>
 hipError_t launch_tile(const Plan& p, const KArgs& a, hipStream_t s) {
   using Cfg = TileCfg<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, PERM, DTL>;
   dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.grid_z);
@@ -1076,11 +1176,14 @@ struct Variant {
                       TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::LDS_BYTES,      \
                       TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::NSETS, 1, PP,   \
                       (TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::A_DTL ? 1 : 0) | \
-                      (TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::B_DTL ? 2 : 0)}, \
+                      (TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::B_DTL ? 2 : 0) | \
+                      (TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::A_TR ? 4 : 0) |  \
+                      (TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::B_TR ? 8 : 0)}, \
           &launch_tile<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, PP, DTL>}
-#define TILE_PP(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, PP) TILE_X(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, PP, false)
-#define TILE(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM) TILE_X(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, false, false)
-#define TILE_DTL(T, AKC, BKC, U4, MTM, MTN, WM, WN) TILE_X(T, AKC, BKC, U4, MTM, MTN, WM, WN, true, false, true)
+#define TILE_PP(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, PP) TILE_X(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, PP, 0)
+#define TILE(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM) TILE_X(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, false, 0)
+#define TILE_DTL(T, AKC, BKC, U4, MTM, MTN, WM, WN) TILE_X(T, AKC, BKC, U4, MTM, MTN, WM, WN, true, false, 1)
+#define TILE_DTLTR(T, AKC, BKC, U4, MTM, MTN, WM, WN) TILE_X(T, AKC, BKC, U4, MTM, MTN, WM, WN, true, false, 2)
 
 #define TILE_LAYOUTS(T, MTM, MTN, WM, WN)                                                    \
   TILE(T, true, true, false, MTM, MTN, WM, WN, true),                                      \
@@ -1093,6 +1196,13 @@ struct Variant {
   TILE_DTL(T, true, true, false, MTM, MTN, WM, WN),                                        \
   TILE_DTL(T, true, false, false, MTM, MTN, WM, WN),                                       \
   TILE_DTL(T, false, true, false, MTM, MTN, WM, WN)
+
+// Layouts with at least one transposed operand, every operand loaded straight into LDS and
+// the transposed ones transposed by the LDS reads.
+#define TILE_LAYOUTS_DTLTR(T, MTM, MTN, WM, WN)                                              \
+  TILE_DTLTR(T, true, false, false, MTM, MTN, WM, WN),                                     \
+  TILE_DTLTR(T, false, true, false, MTM, MTN, WM, WN),                                     \
+  TILE_DTLTR(T, false, false, false, MTM, MTN, WM, WN)
 
 #define TILE_LAYOUTS_PP(T, MTM, MTN, WM, WN)                                                 \
   TILE_PP(T, true, true, false, MTM, MTN, WM, WN, true, true),                             \

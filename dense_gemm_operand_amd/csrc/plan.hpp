@@ -58,7 +58,8 @@ struct VariantInfo {
   int32_t depth;                  // skinny: K iterations in flight per wave
   int32_t slots_per_cu;           // workgroups assumed resident per CU by the split-K search
   int32_t sched;                  // tiled: 0 = software pipeline, 1 = ping-pong wave groups
-  int32_t dtl;                    // tiled: bit 0 A, bit 1 B loaded straight into LDS
+  int32_t dtl;                    // tiled: bit 0 A, bit 1 B loaded straight into LDS;
+                                  // bit 2 A, bit 3 B transposed by the LDS reads
 };
 
 int variant_count();

@@ -86,7 +86,11 @@ typedef struct {
   int32_t direct_lds;      /* bit 0 (A), bit 1 (B): the K-contiguous operand is loaded
                               straight from global memory into LDS (rows of 128 B without
                               padding, 16-byte chunks permuted by an XOR of the row);
-                              lds_pad_bytes then applies to the other operand only */
+                              lds_pad_bytes then applies to the other operand only.
+                              bit 2 (A), bit 3 (B): the transposed operand is also loaded
+                              straight into LDS in global order (1 KiB blocks of two K rows
+                              plus lds_pad_bytes = 64, K rows permuted with perm_block = 8,
+                              perm_stride = 4) and transposed by the LDS reads */
 } gemm_plan_info_t;
 
 /* Make a plan for C (M x N, row-major, dtype_c) = A (M x K) * B (K x N).
@@ -105,6 +109,11 @@ typedef struct {
  * The plan binds to the HIP device current at this call (its CU count feeds the
  * split-K search; the environment variable DGEMM_FAKE_CU_COUNT replaces the query so
  * that planning works without a device). Host only: no allocation, no launch.
+ * Loader for a transposed operand: by default it is transposed in registers with byte
+ * permutes and stored K-contiguous (Triton PR 5223). DGEMM_FORCE_DTL=2 in the environment
+ * selects, for 256x256 tiles, the other loader of the pages (rocm-libraries PR 2487): the
+ * operand goes straight into LDS in global order and is transposed by the LDS reads
+ * (ds_read_b64_tr_b16); gemm_plan_info_t.direct_lds reports which was chosen.
  * On error *out is set to NULL. */
 int gemm_plan(gemm_plan_t* out, int64_t M, int64_t N, int64_t K, int layout_a, int layout_b,
               int dtype_a, int dtype_b, int dtype_c, int split_k, const gemm_quant_t* quant);

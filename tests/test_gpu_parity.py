@@ -273,3 +273,48 @@ def test_int4_skinny_variants_bit_exact(v, sk):
     assert (info["tile_n"], info["waves"]) == (16 * int(v.split("x")[0]), int(v.split("x")[1]))
     _, ref = reference(inp, "f16", "f32", int4=True)
     assert np.array_equal(c, ref)
+
+
+TR_LAYOUTS = [("col", "col"), ("row", "row"), ("col", "row")]   # a transposed operand
+
+
+def _tr_bits(la, lb):
+    # direct_lds bits: 1/2 K-contiguous A/B loaded directly, 4/8 transposed A/B loaded
+    # directly and transposed by the LDS reads
+    return ((1 if la == "row" else 4) | (2 if lb == "col" else 8))
+
+
+@pytest.mark.parametrize("la,lb", TR_LAYOUTS)
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_transposing_lds_reads_integer_bit_exact(la, lb, fmt):
+    # transposed operands kept in global order in padded, K-row-permuted LDS blocks and
+    # transposed by ds_read_b64_tr_b16; ragged M, N and K
+    from helpers import env
+    M, N, K = 392 + 8, 648, 200
+    _say("tr-int", la, lb, fmt)
+    inp = _inputs_int(M, N, K, la, lb, fmt, seed=101)
+    with env(DGEMM_FORCE_DTL=2):
+        c, info = run_gpu(inp, fmt, "f32", split_k=1, force_tile="256x256", guard=64)
+    assert info["direct_lds"] == _tr_bits(la, lb)
+    assert (info["perm_block"], info["perm_stride"], info["lds_pad_bytes"]) == (8, 4, 64)
+    _, ref = reference(inp, fmt, "f32")
+    assert np.array_equal(c, ref)
+
+
+@pytest.mark.parametrize("la,lb", TR_LAYOUTS)
+def test_transposing_lds_reads_split_k_and_random(la, lb):
+    from helpers import env
+    M, N, K = 264, 520, 1032
+    _say("tr-split", la, lb)
+    inp = _inputs_int(M, N, K, la, lb, "f16", seed=103)
+    _, ref = reference(inp, "f16", "f32")
+    with env(DGEMM_FORCE_DTL=2):
+        for sk in (1, 4):
+            c, info = run_gpu(inp, "f16", "f32", split_k=sk, force_tile="256x256", guard=16)
+            assert info["direct_lds"] == _tr_bits(la, lb) and info["split_k"] == sk
+            assert np.array_equal(c, ref), sk
+        inp = _inputs_rand(520, 392, 328, la, lb, "bf16", seed=105)
+        c, _ = run_gpu(inp, "bf16", "bf16", split_k=1, force_tile="256x256", guard=16)
+    _, ref = reference(inp, "bf16", "bf16")
+    amax, bmax = operand_max(inp, "bf16")
+    check_tolerance(c, ref, "bf16", 328, amax, bmax, "tr")
