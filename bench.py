@@ -224,6 +224,50 @@ def stream_context() -> dict:
             "note": "torch sum over 2 GiB fp16 and copy of 1 GiB, events over 5 runs each"}
 
 
+def loader_comparison(rounds: int = 5, calls: int = 20) -> list:
+    """The two loaders for transposed operands on the same shapes, timed interleaved
+    (rounds of `calls` back-to-back launches, alternating) so that clock drift on the box
+    affects both alike: the in-register transpose (default) and direct-to-LDS loads in
+    global order transposed by the LDS reads (planner hook DGEMM_FORCE_DTL=2)."""
+    import torch
+    from dense_gemm_operand_amd import synth
+    res = []
+    for name, la, lb in [("square_4096", "col", "col"), ("square_4096", "row", "row"),
+                         ("square_4096", "col", "row"), ("nonpow2_bf16", None, None)]:
+        wl = synth.WORKLOADS[name]
+        hs = [Gemm(wl, la, lb)]
+        os.environ["DGEMM_FORCE_DTL"] = "2"
+        try:
+            hs.append(Gemm(wl, la, lb))
+        finally:
+            os.environ.pop("DGEMM_FORCE_DTL", None)
+        t = [[], []]
+        for _ in range(rounds):
+            for i, h in enumerate(hs):
+                for _ in range(3):
+                    h.run()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(calls):
+                    h.run()
+                e1.record()
+                torch.cuda.synchronize()
+                t[i].append(e0.elapsed_time(e1) * 1e3 / calls)
+        rec = {"workload": name, "layout_a": hs[0].la, "layout_b": hs[0].lb}
+        for key, h, ts in (("in_register_transpose", hs[0], t[0]), ("transposing_lds_reads", hs[1], t[1])):
+            med = float(np.median(ts))
+            rec[key] = {"us_median": round(med, 2), "tflops": round(h.flops / (med * 1e-6) / 1e12, 1),
+                        "waves": h.info["waves"], "direct_lds": h.info["direct_lds"],
+                        "tile": f"{h.info['tile_m']}x{h.info['tile_n']}"}
+        log(json.dumps(rec))
+        res.append(rec)
+        for h in hs:
+            h.close()
+        del hs
+        torch.cuda.empty_cache()
+    return res
+
+
 def run_workload(name: str, la, lb, steps: int):
     """Only one workload, `steps` launches (rotating input sets for HBM-bound shapes)."""
     import torch
@@ -331,16 +375,12 @@ def main():
 
     if not args.only_headline:
         extra = []
-        # (workload, layouts, bound, planner hooks): the last entries time the other loader
-        # for transposed operands (kept in global order in LDS, transposed by the LDS reads)
-        tr = {"DGEMM_FORCE_DTL": "2"}
+        # (workload, layouts, bound, planner hooks)
         cases = [
             ("square_4096", "row", "row", "mfma", {}), ("square_4096", "col", "row", "mfma", {}),
             ("square_4096", "row", "col", "mfma", {}), ("nonpow2_bf16", None, None, "mfma", {}),
             ("square_tt_256", None, None, "mfma", {}), ("int4_m4096", None, None, "mfma", {}),
             ("skinny_splitk", None, None, "hbm", {}), ("int4_m16", None, None, "hbm", {}),
-            ("square_4096", "col", "col", "mfma", tr), ("square_4096", "row", "row", "mfma", tr),
-            ("square_4096", "col", "row", "mfma", tr), ("nonpow2_bf16", None, None, "mfma", tr),
         ]
         for name, la, lb, bound, hooks in cases:
             wl = synth.WORKLOADS[name]
@@ -375,6 +415,7 @@ def main():
             del h
             torch.cuda.empty_cache()
         out["workloads"] = extra
+        out["loader_comparison"] = loader_comparison()
         out["context"] = stream_context()
     print(json.dumps(out), flush=True)
 
