@@ -1,0 +1,117 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the bench times.
+
+Every workload is planned as bench.py plans it (same seeded inputs, same split-K request,
+so the same kernel, tile and split). Random inputs are checked against the oracle on
+sampled row ranges (first rows, a middle range, last rows: several tiles and the edge),
+to the acceptance bar. Properties that hold at any size are checked on every element of
+the full-size result: a permutation matrix as A (or B) makes C an exact row (or column)
+permutation of the other operand, and unit rows of A make C the exactly dequantised int4
+weight rows."""
+import numpy as np
+import pytest
+
+import oracle
+from dense_gemm_operand_amd import synth
+from helpers import check_tolerance, env, operand_max, reference, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _row_ranges(M: int, n: int = 8):
+    if M <= 3 * n:
+        return [(0, M)]
+    mid = (M // 2) // n * n + n // 2   # off the tile grid
+    return [(0, n), (mid, mid + n), (M - n, M)]
+
+
+def _check_sampled(inp, w, c, what):
+    amax, bmax = operand_max(inp, w.dtype_ab, int4=w.int4)
+    for r0, r1 in _row_ranges(inp["M"]):
+        _, ref = reference(inp, w.dtype_ab, w.dtype_c, int4=w.int4, rows=(r0, r1))
+        check_tolerance(c[r0:r1], ref, w.dtype_c, inp["K"], amax, bmax, f"{what} rows {r0}..{r1}")
+
+
+FULL = [("square_tt_256", None, None), ("square_4096", "col", "col"),
+        ("square_4096", "col", "row"), ("square_4096", "row", "col"),
+        ("square_4096", "row", "row"), ("nonpow2_bf16", None, None),
+        ("skinny_splitk", None, None), ("int4_m16", None, None), ("int4_m4096", None, None)]
+
+
+@pytest.mark.parametrize("name,la,lb", FULL)
+def test_full_size_sampled_rows_against_the_oracle(name, la, lb):
+    w = synth.WORKLOADS[name]
+    _say("full", name, la, lb)
+    inp = synth.make_inputs(w, layout_a=la, layout_b=lb)
+    c, info = run_gpu(inp, w.dtype_ab, w.dtype_c, split_k=w.split_k, int4=w.int4, guard=16)
+    _check_sampled(inp, w, c, name)
+
+
+def test_full_size_split_k_sweep():
+    # the split-K shape with every factor the pages' heuristic can pick, plus the auto choice
+    w = synth.WORKLOADS["skinny_splitk"]
+    inp = synth.make_inputs(w)
+    _, ref = reference(inp, w.dtype_ab, w.dtype_c)
+    amax, bmax = operand_max(inp, w.dtype_ab)
+    for sk in (0, 1, 2, 4, 8, 16):
+        _say("full split-k", sk)
+        c, info = run_gpu(inp, w.dtype_ab, w.dtype_c, split_k=sk, guard=16)
+        assert sk == 0 or info["split_k"] == sk
+        check_tolerance(c, ref, w.dtype_c, inp["K"], amax, bmax, f"split_k={sk}")
+
+
+def _perm_inputs(which: str, la: str, lb: str, seed: int):
+    n = 4096
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(n)
+    other = synth.integer_matrix(rng, n, n, -8, 8, "f16")
+    pm = np.zeros((n, n))
+    pm[np.arange(n), perm] = 1.0
+    pbits = synth.to_bits(pm, "f16")
+    a, b = (pbits, other) if which == "A" else (other, pbits)
+    inp = {"M": n, "N": n, "K": n, "layout_a": la, "layout_b": lb,
+           "A": synth.store(a, la), "B": synth.store(b, lb)}
+    # A = P: C[i, :] = B[perm[i], :]; B = P: C[:, perm[k]] = A[:, k], i.e. C = A[:, inv]
+    if which == "A":
+        want = other[perm]
+    else:
+        inv = np.empty(n, dtype=np.int64)
+        inv[perm] = np.arange(n)
+        want = other[:, inv]
+    return inp, want
+
+
+@pytest.mark.parametrize("which", ["A", "B"])
+@pytest.mark.parametrize("la,lb", [("col", "col"), ("col", "row"), ("row", "col"), ("row", "row")])
+@pytest.mark.parametrize("loader", ["default", "transposing_reads"])
+def test_full_size_permutation_every_element(which, la, lb, loader):
+    # 4096^3 as the bench runs it: every element of C must be the exact permuted entry
+    if loader == "transposing_reads" and la == "row" and lb == "col":
+        pytest.skip("no transposed operand")
+    _say("full perm", which, la, lb, loader)
+    inp, want = _perm_inputs(which, la, lb, seed=111 + (which == "B"))
+    with env(DGEMM_FORCE_DTL=2 if loader == "transposing_reads" else None):
+        c, info = run_gpu(inp, "f16", "f16", split_k=1, guard=16)
+    assert ((info["direct_lds"] & 12) != 0) == (loader == "transposing_reads")
+    assert np.array_equal(c, want)
+
+
+@pytest.mark.parametrize("name", ["int4_m16", "int4_m4096"])
+def test_full_size_int4_unit_rows_give_dequantised_weights(name):
+    # the int4 shapes' own codes and scales; A rows are unit vectors, so each C row is one
+    # dequantised weight row, exactly (one nonzero product per sum)
+    w = synth.WORKLOADS[name]
+    _say("full int4 unit rows", name)
+    inp = synth.make_inputs(w)
+    M, K, N = inp["M"], inp["K"], inp["N"]
+    rng = np.random.default_rng(121)
+    pick = rng.integers(0, K, size=M)
+    a = np.zeros((M, K))
+    a[np.arange(M), pick] = 1.0
+    inp["A"] = synth.store(synth.to_bits(a, "f16"), "row")
+    c, info = run_gpu(inp, "f16", "f16", split_k=w.split_k, int4=True, guard=16)
+    wts = oracle.dequant_u4(inp["B"], inp["scales"], K, N)
+    assert np.array_equal(oracle.decode(c, "f16"), wts[pick])
