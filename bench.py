@@ -67,13 +67,16 @@ def read_traffic():
 class Gemm:
     """One planned GEMM with device operands (and rotation copies for HBM-bound shapes)."""
 
-    def __init__(self, w, layout_a=None, layout_b=None, rotate_bytes=0):
+    def __init__(self, w, layout_a=None, layout_b=None, rotate_bytes=0, b_tiled=False):
         import torch
         import dense_gemm_operand_amd as dg
         from dense_gemm_operand_amd import synth
         self.dg, self.torch, self.w = dg, torch, w
         t0 = time.time()
         inp = synth.make_inputs(w, layout_a=layout_a, layout_b=layout_b)
+        if b_tiled:   # int4 codes repacked into the pre-tiled layout (offline step)
+            inp = dict(inp, B=dg.gemm_pack_u4_tiled(inp["B"], inp["N"], inp["K"]),
+                       layout_b="u4_tiled")
         self.inp = inp
         self.M, self.N, self.K = inp["M"], inp["N"], inp["K"]
         self.la, self.lb = inp["layout_a"], inp["layout_b"]
@@ -268,6 +271,37 @@ def loader_comparison(rounds: int = 5, calls: int = 20) -> list:
     return res
 
 
+def int4_layout_comparison(rounds: int = 5) -> list:
+    """int4 B in the column-major packing and pre-tiled (64 columns x 128 K blocks), timed
+    interleaved: HIP graphs of back-to-back launches over rotating input sets for M = 16,
+    events over back-to-back launches for M = 4096."""
+    import torch
+    from dense_gemm_operand_amd import synth
+    res = []
+    for name in ("int4_m16", "int4_m4096"):
+        wl = synth.WORKLOADS[name]
+        hbm = name == "int4_m16"
+        rot = 2 * MALL_BYTES + (64 << 20) if hbm else 0
+        hs = [Gemm(wl, rotate_bytes=rot), Gemm(wl, rotate_bytes=rot, b_tiled=True)]
+        t = [[], []]
+        for _ in range(rounds):
+            for i, h in enumerate(hs):
+                t[i].append(h.time_graph(32, 5) if hbm else h.time_events(10, 3)[1])
+        rec = {"workload": name, "M": hs[0].M, "N": hs[0].N, "K": hs[0].K}
+        for key, h, ts in (("column_major_codes", hs[0], t[0]), ("pre_tiled_codes", hs[1], t[1])):
+            med = float(np.median(ts))
+            rec[key] = {"us_median": round(med * 1e3, 2), "gbs": round(h.bytes / (med * 1e-3) / 1e9, 1),
+                        "tflops": round(h.flops / (med * 1e-3) / 1e12, 1), "split_k": h.info["split_k"],
+                        "tile": f"{h.info['tile_m']}x{h.info['tile_n']}"}
+        log(json.dumps(rec))
+        res.append(rec)
+        for h in hs:
+            h.close()
+        del hs
+        torch.cuda.empty_cache()
+    return res
+
+
 def run_workload(name: str, la, lb, steps: int):
     """Only one workload, `steps` launches (rotating input sets for HBM-bound shapes)."""
     import torch
@@ -416,6 +450,7 @@ def main():
             torch.cuda.empty_cache()
         out["workloads"] = extra
         out["loader_comparison"] = loader_comparison()
+        out["int4_layout_comparison"] = int4_layout_comparison()
         out["context"] = stream_context()
     print(json.dumps(out), flush=True)
 

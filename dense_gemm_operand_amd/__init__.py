@@ -13,7 +13,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdgemm.so")
 
-GEMM_ROW_MAJOR, GEMM_COL_MAJOR = 0, 1
+GEMM_ROW_MAJOR, GEMM_COL_MAJOR, GEMM_U4_TILED = 0, 1, 2
 GEMM_F32, GEMM_F16, GEMM_BF16, GEMM_U4 = 0, 1, 2, 3
 GEMM_OK = 0
 GEMM_ERR_INVALID_ARG = -1
@@ -23,7 +23,7 @@ GEMM_ERR_WORKSPACE_TOO_SMALL = -4
 GEMM_ERR_NO_DEVICE = -5
 GEMM_ERR_HIP = -6
 
-LAYOUT = {"row": GEMM_ROW_MAJOR, "col": GEMM_COL_MAJOR}
+LAYOUT = {"row": GEMM_ROW_MAJOR, "col": GEMM_COL_MAJOR, "u4_tiled": GEMM_U4_TILED}
 DTYPE = {"f32": GEMM_F32, "f16": GEMM_F16, "bf16": GEMM_BF16, "u4": GEMM_U4}
 
 # Bytes at the start of every workspace that hold arrival counters (must be zero before
@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_status_string.restype = ctypes.c_char_p
         L.gemm_lds_row_perm.argtypes = [i32, i32, i32, i32]
         L.gemm_lds_row_perm.restype = i32
+        L.gemm_pack_u4_tiled.argtypes = [vp, vp, i64, i64]
+        L.gemm_pack_u4_tiled.restype = i32
         _lib = L
     return _lib
 
@@ -169,3 +171,15 @@ def gemm_status_string(status: int) -> str:
 
 def gemm_lds_row_perm(block: int, stride: int, index: int, inverse: bool = False) -> int:
     return lib().gemm_lds_row_perm(block, stride, index, 1 if inverse else 0)
+
+
+def gemm_pack_u4_tiled(codes, N: int, K: int):
+    """Host repack of int4 codes (numpy uint8, N*K/2 bytes, column-major packing) into the
+    pre-tiled layout; returns a new numpy uint8 array."""
+    import numpy as np
+    src = np.ascontiguousarray(codes, dtype=np.uint8)
+    dst = np.empty_like(src)
+    st = lib().gemm_pack_u4_tiled(src.ctypes.data, dst.ctypes.data, N, K)
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm_pack_u4_tiled")
+    return dst

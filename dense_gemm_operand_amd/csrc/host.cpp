@@ -185,7 +185,8 @@ int make_plan(Plan& p, int split_k_req) {
   if (sk > 1 && tiles > kMaxCounters) sk = 1;
   p.split_k = sk;
   // chunk: ceil(K / sk) rounded up to the per-iteration granule of the kernel
-  const int64_t gran = v.kernel == KERNEL_TILE ? v.tile_k : v.tile_k;
+  // int4 splits start on a scale group (the tiled code layout needs whole 128-K groups)
+  const int64_t gran = p.dtype_b == DT_U4 ? 128 : v.tile_k;
   p.k_chunk = cdiv(cdiv(p.K, sk), gran) * gran;
   if (v.kernel == KERNEL_TILE) {
     p.grid_x = tiles;
@@ -224,8 +225,10 @@ int gemm_plan(gemm_plan_t* out, int64_t M, int64_t N, int64_t K, int layout_a, i
   if (!out) return GEMM_ERR_INVALID_ARG;
   *out = nullptr;
   if (M <= 0 || N <= 0 || K <= 0) return GEMM_ERR_INVALID_ARG;
-  if ((layout_a != 0 && layout_a != 1) || (layout_b != 0 && layout_b != 1))
+  if ((layout_a != 0 && layout_a != 1) || (layout_b < 0 || layout_b > 2))
     return GEMM_ERR_INVALID_ARG;
+  const bool b_tiled = layout_b == 2;
+  if (b_tiled && (dtype_b != DT_U4 || N % 64 != 0)) return GEMM_ERR_UNSUPPORTED;
   if (dtype_a < 0 || dtype_a > 3 || dtype_b < 0 || dtype_b > 3 || dtype_c < 0 || dtype_c > 3)
     return GEMM_ERR_INVALID_ARG;
   if (split_k < 0) return GEMM_ERR_INVALID_ARG;
@@ -235,7 +238,7 @@ int gemm_plan(gemm_plan_t* out, int64_t M, int64_t N, int64_t K, int layout_a, i
   if (dtype_a != DT_F16 && dtype_a != DT_BF16) return GEMM_ERR_UNSUPPORTED;
   if (dtype_c == DT_U4) return GEMM_ERR_UNSUPPORTED;
   if (dtype_b == DT_U4) {
-    if (dtype_a != DT_F16 || layout_b != 1 || !quant) return GEMM_ERR_UNSUPPORTED;
+    if (dtype_a != DT_F16 || layout_b == 0 || !quant) return GEMM_ERR_UNSUPPORTED;
     if (quant->group_size != 128 || quant->zero_point != 8 || quant->scale_dtype != DT_F16 ||
         quant->scale_layout != 0)
       return GEMM_ERR_UNSUPPORTED;
@@ -259,7 +262,8 @@ int gemm_plan(gemm_plan_t* out, int64_t M, int64_t N, int64_t K, int layout_a, i
   p.N = N;
   p.K = K;
   p.layout_a = layout_a;
-  p.layout_b = layout_b;
+  p.layout_b = b_tiled ? 1 : layout_b;   // the tiled codes are K-packed like column-major
+  p.b_tiled = b_tiled ? 1 : 0;
   p.dtype_a = dtype_a;
   p.dtype_b = dtype_b;
   p.dtype_c = dtype_c;
@@ -269,6 +273,18 @@ int gemm_plan(gemm_plan_t* out, int64_t M, int64_t N, int64_t K, int layout_a, i
     return st;
   }
   *out = h;
+  return GEMM_OK;
+}
+
+int gemm_pack_u4_tiled(const void* codes, void* tiled, int64_t N, int64_t K) {
+  if (!codes || !tiled || N <= 0 || K <= 0) return GEMM_ERR_INVALID_ARG;
+  if (N % 64 != 0 || K % 128 != 0) return GEMM_ERR_UNSUPPORTED;
+  const uint8_t* src = static_cast<const uint8_t*>(codes);
+  uint8_t* dst = static_cast<uint8_t*>(tiled);
+  const int64_t groups = K / 128;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t g = 0; g < groups; ++g)
+      std::memcpy(dst + ((n / 64) * groups + g) * 4096 + (n % 64) * 64, src + n * (K / 2) + g * 64, 64);
   return GEMM_OK;
 }
 
@@ -311,7 +327,7 @@ int gemm_plan_query(gemm_plan_t plan, gemm_plan_info_t* info) {
   info->N = p.N;
   info->K = p.K;
   info->layout_a = p.layout_a;
-  info->layout_b = p.layout_b;
+  info->layout_b = p.b_tiled ? 2 : p.layout_b;
   info->dtype_a = p.dtype_a;
   info->dtype_b = p.dtype_b;
   info->dtype_c = p.dtype_c;

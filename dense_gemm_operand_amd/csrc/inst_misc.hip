@@ -81,6 +81,7 @@ int launch(const Plan& p, const RunArgs& r, void* stream) {
   a.dtype_c = p.dtype_c;
   const int ob = p.dtype_c == DT_F32 ? 4 : 2;
   a.c_vec = ((p.N * ob) % 16 == 0) ? 1 : 0;
+  a.b_tiled = p.b_tiled;
   if (p.kernel == KERNEL_SKINNY) a.c_vec = (p.N % 4 == 0) ? 1 : 0;  // 4-element stores
   return (int)all_variants()[p.variant]->fn(p, a, reinterpret_cast<hipStream_t>(stream));
 }

@@ -187,6 +187,7 @@ struct KArgs {
   int tiles_m, tiles_n;
   int dtype_c;
   int c_vec;            // 1 if every C row starts 16-byte aligned
+  int b_tiled;          // int4 codes in the pre-tiled layout (64 columns x 128 K blocks)
 };
 
 // Split-K fix-up shared by both kernels. Every thread owns NV vectors of LEN fp32
@@ -291,7 +292,7 @@ struct Operand {
   // Block q of this K split: offsets, K offset and LDS base. Blocks past BLOCKS (idle
   // lanes of a partial slot) read nothing and store into their own dead row.
   __device__ __forceinline__ static void setup(Slot<VPB>& s, int q, int row0, int rows_total,
-                                               int ld, int kb, int K) {
+                                               int ld, int kb, int K, bool tiled = false) {
     const bool live = q < BLOCKS;
     if constexpr (KIND == 0) {
       const int c = q % 8;
@@ -312,7 +313,12 @@ struct Operand {
       s.wbase = P.inv(8 * v) * PITCH_B + 16 * kg + 8 * kh;
     } else {
       const int r = q / 2, h = q % 2;
-      s.off[0] = (live && row0 + r < rows_total) ? (uint32_t)(row0 + r) * (uint32_t)(K / 2) + (uint32_t)((kb + 32 * h) / 2) : kOOB;
+      // column-major packing: byte n*(K/2) + k/2; pre-tiled: 4 KiB blocks of 64 columns x
+      // 128 K, 64 bytes per column (the split start kb is a multiple of 128)
+      const int n = row0 + r;
+      const uint32_t o = tiled ? ((uint32_t)((n / 64) * (K / 128) + kb / 128) * 64u + (uint32_t)(n % 64)) * 64u + 16u * h
+                               : (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)((kb + 32 * h) / 2);
+      s.off[0] = (live && n < rows_total) ? o : kOOB;
       s.kofs = 32 * h;
       s.wbase = P.inv(r) * PITCH_B + 64 * h;
       s.row = row0 + r;
@@ -581,7 +587,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
 #pragma unroll
   for (int i = 0; i < SA; ++i) OpA::setup(sa[i], i * THREADS + tid, m0, a.M, a.ldA, kb, a.K);
 #pragma unroll
-  for (int i = 0; i < SB; ++i) OpB::setup(sb[i], i * THREADS + tid, n0, a.N, a.ldB, kb, a.K);
+  for (int i = 0; i < SB; ++i) OpB::setup(sb[i], i * THREADS + tid, n0, a.N, a.ldB, kb, a.K, a.b_tiled != 0);
   // Byte step of the offsets per K step.
   const uint32_t dA = A_KC ? BK * 2u : (uint32_t)(BK * a.ldA) * 2u;
   const uint32_t dB = U4B ? BK / 2u : (B_KC ? BK * 2u : (uint32_t)(BK * a.ldB) * 2u);
@@ -622,7 +628,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < SB; ++i) {
-      const uint32_t d = dB * (uint32_t)step;
+      // pre-tiled int4 codes: a 64-K step is half of a 4 KiB block's 64-byte rows
+      const uint32_t d = (U4B && a.b_tiled) ? (uint32_t)(step >> 1) * 4096u + (uint32_t)(step & 1) * 32u
+                                            : dB * (uint32_t)step;
 #pragma unroll
       for (int j = J0; j < J1 && j < OpB::VPB; ++j) {
         const bool ok = sb[i].kofs + ((B_KC || U4B) ? 0 : j) < lim;
@@ -1010,14 +1018,18 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int n = n0 + 16 * nb + r;
-      offB0[nb] = (uint32_t)n * (uint32_t)(a.K / 2) + (uint32_t)((kb + c * KL) / 2);
+      // column-major packing: byte n*(K/2) + k/2; pre-tiled: 4 KiB blocks of 64 columns x
+      // 128 K (one iteration), 64 bytes per column
+      offB0[nb] = a.b_tiled ? ((uint32_t)((n / 64) * (a.K / 128) + kb / 128) * 64u + (uint32_t)(n % 64)) * 64u + 16u * c
+                            : (uint32_t)n * (uint32_t)(a.K / 2) + (uint32_t)((kb + c * KL) / 2);
       offS0[nb] = ((uint32_t)(kb / 128) * (uint32_t)a.N + (uint32_t)n) * 2u;
     }
   }
+  const uint32_t b_iter = a.b_tiled ? 4096u : (uint32_t)(KI / 2);   // B bytes per iteration
   auto load = [&](int u, int j) {
     const int it = wave + j * W;
     if constexpr (U4B) {
-      const uint32_t sa = (uint32_t)it * KI * 2u, sb = (uint32_t)it * (KI / 2);
+      const uint32_t sa = (uint32_t)it * KI * 2u, sb = (uint32_t)it * b_iter;
       const uint32_t ss = (uint32_t)it * (uint32_t)a.N * 2u;
 #pragma unroll
       for (int h = 0; h < H; ++h)

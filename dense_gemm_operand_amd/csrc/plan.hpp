@@ -29,6 +29,7 @@ struct Plan {
   int32_t cu_count = 0;
   int32_t slots_per_cu = 1;
   int32_t direct_lds = 0;              // bit 0: A, bit 1: B loaded straight into LDS
+  int32_t b_tiled = 0;                 // int4 codes in the pre-tiled layout (layout_b 2)
   int32_t device = -1;
 };
 

@@ -33,8 +33,14 @@ extern "C" {
 
 /* Storage order of a logical matrix (A is M x K, B is K x N). Row-major: element (r, c)
  * at r * cols + c. Column-major: element (r, c) at r + c * rows. Storage is packed (no
- * leading dimension). */
-enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1 };
+ * leading dimension).
+ * GEMM_U4_TILED (int4 B only) is the pre-tiled weight layout of BitBLAS PR 268 (its
+ * tiled/"ladder" weight transform): the 64 code bytes of column n and K group g (the
+ * 128 codes k = 128g .. 128g+127, low nibble = even k) are stored at byte
+ * ((n / 64) * (K / 128) + g) * 4096 + (n % 64) * 64, so every 64 columns x 128 K block is
+ * one contiguous 4 KiB run and a workgroup's share of B is one contiguous range.
+ * gemm_pack_u4_tiled() converts from the column-major packing. Needs N % 64 == 0. */
+enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1, GEMM_U4_TILED = 2 };
 
 /* Element types. GEMM_U4 is valid for B only: two 4-bit codes per byte along K. */
 enum { GEMM_F32 = 0, GEMM_F16 = 1, GEMM_BF16 = 2, GEMM_U4 = 3 };
@@ -97,8 +103,8 @@ typedef struct {
  *
  * layout_a/layout_b: GEMM_ROW_MAJOR or GEMM_COL_MAJOR storage of the logical operands.
  * dtype_a: GEMM_F16 or GEMM_BF16. dtype_b: the same as dtype_a, or GEMM_U4 with
- *   dtype_a == GEMM_F16, layout_b == GEMM_COL_MAJOR (codes packed along K) and a
- *   non-null `quant` (otherwise quant must be NULL or is ignored).
+ *   dtype_a == GEMM_F16, layout_b == GEMM_COL_MAJOR (codes packed along K) or
+ *   GEMM_U4_TILED, and a non-null `quant` (otherwise quant must be NULL or is ignored).
  * dtype_c: GEMM_F32, GEMM_F16 or GEMM_BF16 (round-to-nearest-even from fp32 sums).
  * split_k: 0 lets the planner choose (waste-ratio search over the workgroup slots,
  *   i.e. CU count times resident workgroups per CU, BitBLAS PR 268 "SplitK Infer",
@@ -117,6 +123,13 @@ typedef struct {
  * On error *out is set to NULL. */
 int gemm_plan(gemm_plan_t* out, int64_t M, int64_t N, int64_t K, int layout_a, int layout_b,
               int dtype_a, int dtype_b, int dtype_c, int split_k, const gemm_quant_t* quant);
+
+/* Host-side repack of int4 codes from the column-major packing (byte n*(K/2) + k/2) into
+ * GEMM_U4_TILED (BitBLAS PR 268, tiled weight transform): `codes` and `tiled` are host
+ * buffers of N*K/2 bytes each, not overlapping; the scales keep their [K/128][N] layout.
+ * Needs N % 64 == 0 and K % 128 == 0 (GEMM_ERR_UNSUPPORTED otherwise), non-null pointers
+ * and positive sizes (GEMM_ERR_INVALID_ARG). */
+int gemm_pack_u4_tiled(const void* codes, void* tiled, int64_t N, int64_t K);
 
 /* Bytes of device workspace gemm_run needs for this plan (0 when split_k == 1). */
 int gemm_workspace_size(gemm_plan_t plan, size_t* bytes);

@@ -20,13 +20,13 @@ HEADER = os.path.join(ROOT, "include", "dgemm.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gemm_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gemm_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted([
         "gemm_plan", "gemm_workspace_size", "gemm_run", "gemm_plan_query",
-        "gemm_plan_destroy", "gemm_status_string", "gemm_lds_row_perm"])
+        "gemm_plan_destroy", "gemm_status_string", "gemm_lds_row_perm", "gemm_pack_u4_tiled"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -204,3 +204,45 @@ def test_direct_to_lds_plans(fake_cus, la, lb, bits):
     with env(DGEMM_FORCE_DTL=1):   # both operands transposed: nothing to load directly
         with pytest.raises(dg.GemmError):
             dg.gemm_plan(4096, 4096, 4096, COL, ROW, F16, F16, F16, 0)
+
+
+def test_pack_u4_tiled_places_every_group_of_every_column():
+    # codes of column n, K group g (64 bytes of the column-major packing) go to the 4 KiB
+    # block (n/64, g) at row n%64; every source byte lands exactly once
+    N, K = 192, 384
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 256, size=N * K // 2, dtype=np.uint8)
+    tiled = dg.gemm_pack_u4_tiled(codes, N, K)
+    G = K // 128
+    src = codes.reshape(N, G, 64)
+    blocks = tiled.reshape(N // 64, G, 64, 64)
+    for n in range(N):
+        for g in range(G):
+            assert np.array_equal(blocks[n // 64, g, n % 64], src[n, g]), (n, g)
+    # a bijection on bytes: tagging every byte with its own index shows each moved once
+    idx = np.arange(N * K // 2)
+    moved = dg.gemm_pack_u4_tiled((idx % 251).astype(np.uint8), N, K)
+    assert np.array_equal(np.sort(moved), np.sort((idx % 251).astype(np.uint8)))
+
+
+def test_pack_u4_tiled_errors():
+    L = dg.lib()
+    buf = np.zeros(64 * 64, dtype=np.uint8)
+    assert L.gemm_pack_u4_tiled(None, buf.ctypes.data, 64, 128) == dg.GEMM_ERR_INVALID_ARG
+    assert L.gemm_pack_u4_tiled(buf.ctypes.data, buf.ctypes.data, 0, 128) == dg.GEMM_ERR_INVALID_ARG
+    assert L.gemm_pack_u4_tiled(buf.ctypes.data, buf.ctypes.data, 32, 128) == dg.GEMM_ERR_UNSUPPORTED
+    assert L.gemm_pack_u4_tiled(buf.ctypes.data, buf.ctypes.data, 64, 64) == dg.GEMM_ERR_UNSUPPORTED
+
+
+def test_tiled_int4_plans(fake_cus):
+    q = dg.int4_quant()
+    T = dg.GEMM_U4_TILED
+    assert _plan_status(16, 8192, 8192, ROW, T, F16, U4, F16, 0, quant=q)[0] == dg.GEMM_OK
+    assert _plan_status(16, 8008, 8192, ROW, T, F16, U4, F16, 0, quant=q)[0] == dg.GEMM_ERR_UNSUPPORTED
+    assert _plan_status(64, 64, 64, ROW, T, F16, F16, F16, 0)[0] == dg.GEMM_ERR_UNSUPPORTED
+    assert _plan_status(64, 64, 64, ROW, 3, F16, F16, F16, 0)[0] == dg.GEMM_ERR_INVALID_ARG
+    for M in (16, 4096):
+        p = dg.gemm_plan(M, 8192, 8192, ROW, T, F16, U4, F16, 0, q)
+        i = dg.gemm_plan_query(p)
+        dg.gemm_plan_destroy(p)
+        assert i["layout_b"] == T and i["kernel"] == (1 if M == 16 else 0)

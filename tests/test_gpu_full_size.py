@@ -115,3 +115,26 @@ def test_full_size_int4_unit_rows_give_dequantised_weights(name):
     c, info = run_gpu(inp, "f16", "f16", split_k=w.split_k, int4=True, guard=16)
     wts = oracle.dequant_u4(inp["B"], inp["scales"], K, N)
     assert np.array_equal(oracle.decode(c, "f16"), wts[pick])
+
+
+@pytest.mark.parametrize("name", ["int4_m16", "int4_m4096"])
+def test_full_size_int4_tiled_layout(name):
+    # the int4 shapes with their codes pre-tiled: sampled rows against the oracle (which reads
+    # the column-major packing) and unit rows giving the exact dequantised weights
+    import dense_gemm_operand_amd as dg
+    w = synth.WORKLOADS[name]
+    _say("full int4 tiled", name)
+    inp = synth.make_inputs(w)
+    M, K, N = inp["M"], inp["K"], inp["N"]
+    tiled = dict(inp, B=dg.gemm_pack_u4_tiled(inp["B"], N, K), layout_b="u4_tiled")
+    c, info = run_gpu(tiled, "f16", "f16", split_k=w.split_k, int4=True, guard=16)
+    assert info["layout_b"] == dg.GEMM_U4_TILED
+    _check_sampled(inp, w, c, name + " tiled")
+    rng = np.random.default_rng(141)
+    pick = rng.integers(0, K, size=M)
+    a = np.zeros((M, K))
+    a[np.arange(M), pick] = 1.0
+    tiled["A"] = synth.store(synth.to_bits(a, "f16"), "row")
+    c, _ = run_gpu(tiled, "f16", "f16", split_k=w.split_k, int4=True, guard=16)
+    wts = oracle.dequant_u4(inp["B"], inp["scales"], K, N)
+    assert np.array_equal(oracle.decode(c, "f16"), wts[pick])

@@ -318,3 +318,27 @@ def test_transposing_lds_reads_split_k_and_random(la, lb):
     _, ref = reference(inp, "bf16", "bf16")
     amax, bmax = operand_max(inp, "bf16")
     check_tolerance(c, ref, "bf16", 328, amax, bmax, "tr")
+
+
+@pytest.mark.parametrize("v,M", [("4x16x2", 5), ("2x8x4", 5), ("8x8x2", 16), ("tile", 384)])
+@pytest.mark.parametrize("sk", [1, 4])
+def test_int4_tiled_layout_bit_exact(v, M, sk):
+    # the same codes packed by gemm_pack_u4_tiled; the oracle reads the column-major packing.
+    # Integer activations and power-of-two scales make every sum exact
+    from helpers import env
+    import dense_gemm_operand_amd as dg
+    N, K = 192, 2048
+    _say("int4-tiled", v, M, sk)
+    inp = _int4_inputs(M, N, K, seed=131)
+    rng = np.random.default_rng(132)
+    inp["A"] = synth.store(synth.integer_matrix(rng, M, K, -2, 2, "f16"), "row")
+    e = rng.integers(2, 7, size=(K // 128) * N)
+    inp["scales"] = synth.to_bits(np.ldexp(1.0, -e), "f16").reshape(-1)
+    _, ref = reference(inp, "f16", "f32", int4=True)
+    tiled = dict(inp, B=dg.gemm_pack_u4_tiled(inp["B"], N, K), layout_b="u4_tiled")
+    hooks = {"DGEMM_FORCE_SKINNY": v} if v != "tile" else {}
+    with env(**hooks):
+        c, info = run_gpu(tiled, "f16", "f32", split_k=sk, int4=True, guard=8)
+    assert info["layout_b"] == dg.GEMM_U4_TILED and info["split_k"] == sk
+    assert info["kernel"] == (0 if v == "tile" else 1)
+    assert np.array_equal(c, ref)
