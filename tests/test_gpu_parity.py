@@ -342,3 +342,23 @@ def test_int4_tiled_layout_bit_exact(v, M, sk):
     assert info["layout_b"] == dg.GEMM_U4_TILED and info["split_k"] == sk
     assert info["kernel"] == (0 if v == "tile" else 1)
     assert np.array_equal(c, ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 8, 16), (24, 40, 8), (264, 8, 72), (8, 520, 136)])
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+@pytest.mark.parametrize("dtl", [1, 2])
+def test_direct_to_lds_mostly_out_of_range_tiles(M, N, K, la, lb, dtl):
+    # one 256x256 tile almost entirely past M, N or K: the out-of-range direct-to-LDS loads
+    # must leave zeros (or be ignored) and the partial steps must add nothing
+    from helpers import env
+    if dtl == 1 and (la, lb) == ("col", "row"):
+        pytest.skip("no K-contiguous operand")
+    if dtl == 2 and (la, lb) == ("row", "col"):
+        pytest.skip("no transposed operand")
+    _say("dtl-edge", M, N, K, la, lb, dtl)
+    inp = _inputs_int(M, N, K, la, lb, "f16", seed=151)
+    with env(DGEMM_FORCE_DTL=dtl):
+        c, info = run_gpu(inp, "f16", "f32", split_k=1, force_tile="256x256", guard=32)
+    assert info["direct_lds"] != 0
+    _, ref = reference(inp, "f16", "f32")
+    assert np.array_equal(c, ref)
