@@ -13,6 +13,7 @@ fp64 in the order A, B, codes, scales, then converted once to the storage format
   int4_m16/int4_m4096  M x 8192 x 8192, A fp16 row-major N(0,1); B 4-bit codes U{0..15}
                     packed two per byte along K (low nibble = even k), zero point 8,
                     fp16 scales [K/128][N] U[0.005, 0.02]; fp16 C
+  square_4096_f8    4096^3 8-bit E4M3 (OCP) operands, BLAS NN storage, N(0, 1), fp16 C
 """
 from __future__ import annotations
 
@@ -51,6 +52,8 @@ WORKLOADS = {
                          int4=True),
     "int4_m4096": Workload("int4_m4096", 4, 4096, 8192, 8192, "row", "col", "f16", "f16", "int4",
                            int4=True, split_k=1),
+    "square_4096_f8": Workload("square_4096_f8", 5, 4096, 4096, 4096, "col", "col", "f8", "f16",
+                               "normal1", split_k=1),
 }
 
 LAYOUT_LETTERS = {  # BLAS column-major lettering -> (A storage, B storage)
@@ -59,10 +62,15 @@ LAYOUT_LETTERS = {  # BLAS column-major lettering -> (A storage, B storage)
 
 
 def to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
-    """fp64 -> storage bits (uint16 for f16/bf16) with the library conversions of numpy
-    (binary16) and torch (bfloat16)."""
+    """fp64 -> storage bits (uint16 for f16/bf16, uint8 for f8) with the library
+    conversions of numpy (binary16) and torch (bfloat16, and float8_e4m3fn for f8: the
+    E4M3 format in the OCP convention)."""
     if dtype == "f16":
         return x.astype(np.float16).view(np.uint16)
+    if dtype == "f8":
+        import torch
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.float8_e4m3fn)
+        return t.view(torch.uint8).numpy()
     if dtype == "bf16":
         import torch
         t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)

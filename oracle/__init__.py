@@ -10,6 +10,8 @@ Contents and the passage each follows:
                            rounding). Non-TN operands: Triton PR 5223, "Feature
                            description"; int4 weights: BitBLAS PR 268, dequantize example.
   * ``dequant_u4``      -- (q - zero) * s rounded once to binary16.
+  * ``decode(.., "f8")`` -- 8-bit E4M3 operands (OCP convention: bias 7, no infinity,
+                           one NaN pattern per sign), exact in fp64.
   * ``splitk_factor``   -- BitBLAS PR 268, "SplitK Infer" code block, with ceil grid.
   * ``perm_fwd/perm_inv`` -- rocm-libraries PR 2487, "Add support for permuting perpDim",
                            forward and inverse mapping formulas.
@@ -29,7 +31,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-FMT = {"f16": 0, "bf16": 1, "f32": 2}
+FMT = {"f16": 0, "bf16": 1, "f32": 2, "f8": 3}   # f8: E4M3 (OCP), decode only
 
 
 def build(force: bool = False) -> str:
@@ -76,8 +78,9 @@ def threads() -> int:
 
 
 def decode(bits: np.ndarray, fmt: str) -> np.ndarray:
-    """Stored bit patterns (uint16 for f16/bf16, uint32 for f32) -> exact fp64 values."""
-    want = np.uint32 if fmt == "f32" else np.uint16
+    """Stored bit patterns (uint16 for f16/bf16, uint32 for f32, uint8 for the fp8 E4M3
+    format) -> exact fp64 values."""
+    want = np.uint32 if fmt == "f32" else (np.uint8 if fmt == "f8" else np.uint16)
     b = np.ascontiguousarray(bits).view(want) if bits.dtype != want else np.ascontiguousarray(bits)
     out = np.empty(b.size, dtype=np.float64)
     if _L().oracle_decode(b.ctypes.data, b.size, FMT[fmt], _dp(out)):

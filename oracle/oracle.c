@@ -17,7 +17,11 @@
  * Split-K, tiling, LDS layouts and permutations are tactics that do not change this
  * definition, so none of them appears here.
  *
- * Format codes used by this file only: 0 = binary16, 1 = bfloat16, 2 = binary32.
+ * Format codes used by this file only: 0 = binary16, 1 = bfloat16, 2 = binary32,
+ * 3 = 8-bit floating point E4M3 in the OCP convention (the fp8 operand format of gfx950's
+ * matrix cores): sign, 4 exponent bits with bias 7, 3 fraction bits; exponent 0 is the
+ * subnormal binade; there is no infinity, and only S.1111.111 is NaN, so the top
+ * exponent is an ordinary binade reaching 448.
  */
 #include <math.h>
 #include <stdint.h>
@@ -94,8 +98,24 @@ static uint32_t encode_bits(double x, fmt_t f) {
   return sign | ((uint32_t)(E + bias) << f.mant_bits) | m;
 }
 
-/* Decode n stored values of format `code` (16-bit codes read uint16, binary32 reads uint32). */
+/* One E4M3 (OCP) value from its byte, from the format's definition above. */
+static double decode_e4m3(uint8_t b) {
+  const int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+  double v;
+  if (e == 15 && m == 7) v = NAN;
+  else if (e == 0) v = ldexp((double)m, -6 - 3);          /* 0.m * 2^(1 - 7) */
+  else v = ldexp((double)(8 + m), e - 7 - 3);             /* 1.m * 2^(e - 7) */
+  return s ? -v : v;
+}
+
+/* Decode n stored values of format `code` (16-bit codes read uint16, binary32 reads
+ * uint32, E4M3 reads bytes). */
 int oracle_decode(const void* src, int64_t n, int code, double* dst) {
+  if (code == 3) {
+    const uint8_t* s = (const uint8_t*)src;
+    for (int64_t i = 0; i < n; ++i) dst[i] = decode_e4m3(s[i]);
+    return 0;
+  }
   fmt_t f;
   if (fmt_of(code, &f)) return -1;
   if (code == 2) {

@@ -270,3 +270,44 @@ def test_splitk_factor_hand_cases():
         lhs, want = ln.split("->")
         cus, M, N, K, bm, bn, bk = map(int, lhs.split())
         assert oracle.splitk_factor(M, N, K, bm, bn, bk, cus) == int(want), ln
+
+
+def test_fp8_e4m3_decode_matches_torch_for_every_code():
+    # all 256 byte patterns against torch's float8_e4m3fn (OCP E4M3) conversion
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    v = oracle.decode(codes, "f8")
+    t = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(v), np.isnan(t))
+    assert np.array_equal(v[~np.isnan(v)], t[~np.isnan(t)])
+    assert np.array_equal(np.signbit(v[~np.isnan(v)]), np.signbit(t[~np.isnan(t)]))
+
+
+def test_fp8_e4m3_closed_form_values():
+    v = oracle.decode(np.arange(256, dtype=np.uint8), "f8")
+    assert v[0x38] == 1.0 and v[0xB8] == -1.0 and v[0x40] == 2.0 and v[0xC0] == -2.0
+    assert v[0x7E] == 448.0 and v[0xFE] == -448.0               # largest finite
+    assert v[0x77] == 240.0 and v[0x30] == 0.5 and v[0x3C] == 1.5
+    assert v[0x08] == 2.0 ** -6 and v[0x01] == 2.0 ** -9        # smallest normal, subnormal
+    assert v[0x00] == 0.0 and not np.signbit(v[0x00]) and np.signbit(v[0x80])
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and np.isnan(v).sum() == 2
+    assert len(set(v[~np.isnan(v)].tolist())) == 253            # +0 and -0 compare equal
+    pos = v[0x00:0x7F]
+    assert np.all(np.diff(pos) > 0)                             # codes ordered by value
+    # integers 0..16 are exact
+    for i in range(17):
+        assert i in set(pos.tolist())
+
+
+def test_fp8_gemm_with_integer_entries_is_the_integer_product():
+    rng = np.random.default_rng(9)
+    M, N, K = 5, 7, 33
+    ai = rng.integers(-8, 9, size=(M, K))
+    bi = rng.integers(-8, 9, size=(K, N))
+    for la in ("row", "col"):
+        for lb in ("row", "col"):
+            a = synth.to_bits(ai.astype(np.float64), "f8")
+            b = synth.to_bits(bi.astype(np.float64), "f8")
+            c64, _ = oracle.gemm(synth.store(a, la), synth.store(b, lb), M, N, K, la, lb,
+                                 "f8", "f32")
+            assert np.array_equal(c64, (ai @ bi).astype(np.float64))
