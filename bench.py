@@ -8,7 +8,8 @@ Prints one JSON line: the headline TFLOP/s, a roofline object for the GEMM kerne
 (algorithmic 2*M*N*K flops per launch over the average launch duration measured with
 HIP events on the launch stream), the CPU oracle's throughput on a bounded sample of
 the same product, and the other workloads (other layouts, the non-power-of-2 bf16
-GEMM, skinny split-K and int4 shapes in GB/s) under "workloads".
+GEMM, skinny split-K and int4 shapes in GB/s, the fp8 E4M3 4096^3 GEMM against the fp8
+matrix peak) under "workloads".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only-headline]
        python bench.py --copy-probe   (plain device copy of known size, for scaling
@@ -31,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 matrix peak
+PEAK_F8_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak
 PEAK_GBS = 8000.0         # MI355X HBM3E
 MALL_BYTES = 256 << 20    # Infinity Cache: HBM-bound timings rotate over more than 2x this
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_square_4096_nn.txt")
@@ -415,6 +417,7 @@ def main():
             ("square_4096", "row", "col", "mfma", {}), ("nonpow2_bf16", None, None, "mfma", {}),
             ("square_tt_256", None, None, "mfma", {}), ("int4_m4096", None, None, "mfma", {}),
             ("skinny_splitk", None, None, "hbm", {}), ("int4_m16", None, None, "hbm", {}),
+            ("square_4096_f8", None, None, "mfma", {}), ("square_4096_f8", "row", "col", "mfma", {}),
         ]
         for name, la, lb, bound, hooks in cases:
             wl = synth.WORKLOADS[name]
@@ -440,7 +443,8 @@ def main():
                               "in-register transpose" if (h.la == "col" or h.lb == "row") else
                               "K-contiguous"),
                    "direct_lds": h.info["direct_lds"], "waves": h.info["waves"]}
-            rec["pct_peak"] = round(100 * (rec["tflops"] / PEAK_TFLOPS if bound == "mfma"
+            peak = PEAK_F8_TFLOPS if wl.dtype_ab == "f8" else PEAK_TFLOPS
+            rec["pct_peak"] = round(100 * (rec["tflops"] / peak if bound == "mfma"
                                            else rec["gbs"] / PEAK_GBS), 2)
             rec["bound"] = bound
             log(json.dumps(rec))

@@ -14,7 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdgemm.so")
 
 GEMM_ROW_MAJOR, GEMM_COL_MAJOR, GEMM_U4_TILED = 0, 1, 2
-GEMM_F32, GEMM_F16, GEMM_BF16, GEMM_U4 = 0, 1, 2, 3
+GEMM_F32, GEMM_F16, GEMM_BF16, GEMM_U4, GEMM_F8 = 0, 1, 2, 3, 4
 GEMM_OK = 0
 GEMM_ERR_INVALID_ARG = -1
 GEMM_ERR_UNSUPPORTED = -2
@@ -24,7 +24,7 @@ GEMM_ERR_NO_DEVICE = -5
 GEMM_ERR_HIP = -6
 
 LAYOUT = {"row": GEMM_ROW_MAJOR, "col": GEMM_COL_MAJOR, "u4_tiled": GEMM_U4_TILED}
-DTYPE = {"f32": GEMM_F32, "f16": GEMM_F16, "bf16": GEMM_BF16, "u4": GEMM_U4}
+DTYPE = {"f32": GEMM_F32, "f16": GEMM_F16, "bf16": GEMM_BF16, "u4": GEMM_U4, "f8": GEMM_F8}
 
 # Bytes at the start of every workspace that hold arrival counters (must be zero before
 # a workspace is first used; every completed run leaves them zero).
@@ -115,7 +115,7 @@ def _nbytes(x) -> int:
 def gemm_plan(M: int, N: int, K: int, layout_a, layout_b, dtype_a, dtype_b, dtype_c,
               split_k: int = 0, quant: gemm_quant_t | None = None) -> int:
     """Make a plan; returns the opaque handle (an int). Layouts: "row"/"col" or codes;
-    dtypes: "f32"/"f16"/"bf16"/"u4" or codes."""
+    dtypes: "f32"/"f16"/"bf16"/"u4"/"f8" or codes."""
     h = ctypes.c_void_p()
     q = ctypes.byref(quant) if quant is not None else None
     st = lib().gemm_plan(ctypes.byref(h), M, N, K, _code(layout_a, LAYOUT), _code(layout_b, LAYOUT),

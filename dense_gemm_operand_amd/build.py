@@ -21,7 +21,7 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument"]
-SOURCES = ["inst_f16.hip", "inst_bf16.hip", "inst_misc.hip", "host.cpp"]
+SOURCES = ["inst_f16.hip", "inst_bf16.hip", "inst_f8.hip", "inst_misc.hip", "host.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -154,8 +154,11 @@ int make_plan(Plan& p, int split_k_req) {
   p.wave_split_k = v.wave_split_k;
   p.lds_pad = 16;
   const bool transposed = (p.layout_a == 1) || (p.layout_b == 0 && p.dtype_b != DT_U4);
-  p.perm_block = (v.kernel == KERNEL_TILE && v.perm && transposed) ? 64 : 1;
-  p.perm_stride = p.perm_block > 1 ? 8 : 1;
+  // row permutation of operands transposed in registers: 64 rows, stride 8 (16-bit) or
+  // 256 rows, stride 16 (fp8)
+  const bool f8 = p.dtype_a == DT_F8;
+  p.perm_block = (v.kernel == KERNEL_TILE && v.perm && transposed) ? (f8 ? 256 : 64) : 1;
+  p.perm_stride = p.perm_block > 1 ? (f8 ? 16 : 8) : 1;
   p.lds_bytes = v.lds_bytes;
   p.slots_per_cu = v.slots_per_cu;
   p.direct_lds = v.kernel == KERNEL_TILE ? v.dtl : 0;
@@ -229,14 +232,14 @@ int gemm_plan(gemm_plan_t* out, int64_t M, int64_t N, int64_t K, int layout_a, i
     return GEMM_ERR_INVALID_ARG;
   const bool b_tiled = layout_b == 2;
   if (b_tiled && (dtype_b != DT_U4 || N % 64 != 0)) return GEMM_ERR_UNSUPPORTED;
-  if (dtype_a < 0 || dtype_a > 3 || dtype_b < 0 || dtype_b > 3 || dtype_c < 0 || dtype_c > 3)
+  if (dtype_a < 0 || dtype_a > 4 || dtype_b < 0 || dtype_b > 4 || dtype_c < 0 || dtype_c > 4)
     return GEMM_ERR_INVALID_ARG;
   if (split_k < 0) return GEMM_ERR_INVALID_ARG;
   if (split_k != 0 && split_k != 1 && split_k != 2 && split_k != 4 && split_k != 8 &&
       split_k != 16)
     return GEMM_ERR_UNSUPPORTED;
-  if (dtype_a != DT_F16 && dtype_a != DT_BF16) return GEMM_ERR_UNSUPPORTED;
-  if (dtype_c == DT_U4) return GEMM_ERR_UNSUPPORTED;
+  if (dtype_a != DT_F16 && dtype_a != DT_BF16 && dtype_a != DT_F8) return GEMM_ERR_UNSUPPORTED;
+  if (dtype_c == DT_U4 || dtype_c == DT_F8) return GEMM_ERR_UNSUPPORTED;
   if (dtype_b == DT_U4) {
     if (dtype_a != DT_F16 || layout_b == 0 || !quant) return GEMM_ERR_UNSUPPORTED;
     if (quant->group_size != 128 || quant->zero_point != 8 || quant->scale_dtype != DT_F16 ||
@@ -246,14 +249,15 @@ int gemm_plan(gemm_plan_t* out, int64_t M, int64_t N, int64_t K, int layout_a, i
   } else if (dtype_b != dtype_a) {
     return GEMM_ERR_UNSUPPORTED;
   }
-  // contiguous extents: multiples of 8 elements (16 bytes)
+  // contiguous extents: multiples of 16 bytes (8 16-bit or 16 fp8 elements)
+  const int64_t eb = dtype_a == DT_F8 ? 1 : 2;
   const int64_t ca = layout_a == 0 ? K : M;
   const int64_t cb = dtype_b == DT_U4 ? K : (layout_b == 0 ? N : K);
-  if (ca % 8 != 0 || cb % 8 != 0) return GEMM_ERR_UNSUPPORTED;
+  if ((ca * eb) % 16 != 0 || (cb * eb) % 16 != 0) return GEMM_ERR_UNSUPPORTED;
   // 32-bit buffer offsets: every operand below 2 GiB, every size within int range
   const int64_t lim = (int64_t)1 << 31;
   const int64_t ob = dtype_c == DT_F32 ? 4 : 2;
-  if (M * K * 2 >= lim - 16 || N * K * 2 >= lim - 16 || M * N * ob >= lim) return GEMM_ERR_UNSUPPORTED;
+  if (M * K * eb >= lim - 16 || N * K * eb >= lim - 16 || M * N * ob >= lim) return GEMM_ERR_UNSUPPORTED;
 
   gemm_plan_s* h = new (std::nothrow) gemm_plan_s;
   if (!h) return GEMM_ERR_INVALID_ARG;

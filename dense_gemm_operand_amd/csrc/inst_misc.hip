@@ -45,7 +45,7 @@ namespace {
 const std::vector<const Variant*>& all_variants() {
   static const std::vector<const Variant*> v = [] {
     std::vector<const Variant*> r;
-    for (auto f : {variants_misc, variants_f16, variants_bf16}) {
+    for (auto f : {variants_misc, variants_f16, variants_bf16, variants_f8}) {
       const Variant* t = nullptr;
       const int n = f(&t);
       for (int i = 0; i < n; ++i) r.push_back(t + i);
@@ -72,8 +72,9 @@ int launch(const Plan& p, const RunArgs& r, void* stream) {
   a.K = (int)p.K;
   a.ldA = (int)(p.layout_a == 0 ? p.K : p.M);
   a.ldB = (int)(p.layout_b == 0 ? p.N : p.K);
-  a.bytesA = (uint32_t)(p.M * p.K * 2);
-  a.bytesB = (uint32_t)(p.dtype_b == DT_U4 ? p.N * p.K / 2 : p.N * p.K * 2);
+  const int64_t eb = p.dtype_a == DT_F8 ? 1 : 2;   // operand element bytes
+  a.bytesA = (uint32_t)(p.M * p.K * eb);
+  a.bytesB = (uint32_t)(p.dtype_b == DT_U4 ? p.N * p.K / 2 : p.N * p.K * eb);
   a.bytesS = (uint32_t)(p.dtype_b == DT_U4 ? (p.K / 128) * p.N * 2 : 0);
   a.k_chunk = (int)p.k_chunk;
   a.tiles_m = (int)((p.M + p.tile_m - 1) / p.tile_m);

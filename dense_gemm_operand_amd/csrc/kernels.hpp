@@ -52,6 +52,12 @@ constexpr uint32_t kOOB = 0x80000000u;
 
 struct F16T {};
 struct BF16T {};
+struct F8T {};   // OCP 8-bit E4M3 (bias 7, no infinities, S.1111.111 is NaN)
+
+// Bytes per operand element; every main-loop step moves 128-byte LDS rows, i.e. 64 K
+// indices of a 16-bit type or 128 of fp8.
+template <class T>
+constexpr int elem_bytes() { return std::is_same<T, F8T>::value ? 1 : 2; }
 
 template <class T>
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c);
@@ -93,6 +99,22 @@ __device__ __forceinline__ u32x2 transpose_row4(const u32x4 (&in)[4], int e) {
   r[0] = __builtin_amdgcn_perm(in[1][e >> 1], in[0][e >> 1], sel);
   r[1] = __builtin_amdgcn_perm(in[3][e >> 1], in[2][e >> 1], sel);
   return r;
+}
+
+// 4x4 block of bytes (fp8 values): r0..r3 are K rows 0..3, byte e of each holds element
+// e along M/N. Out o[e] holds element e for K rows 0..3 (byte j = K row j). The same byte
+// permute transpose as for 16-bit values, at byte granularity: the first pair of permutes
+// interleaves the bytes of rows (0, 1) and (2, 3), the second joins the 16-bit halves.
+__device__ __forceinline__ void transpose_bytes4(uint32_t r0, uint32_t r1, uint32_t r2,
+                                                 uint32_t r3, uint32_t (&o)[4]) {
+  const uint32_t t0 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);  // r0.b0 r1.b0 r0.b1 r1.b1
+  const uint32_t t1 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);  // r0.b2 r1.b2 r0.b3 r1.b3
+  const uint32_t t2 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
+  const uint32_t t3 = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
+  o[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  o[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  o[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  o[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
 }
 
 // Eight 4-bit codes of one dword (byte b: low nibble = code of K index 2b, high nibble =
@@ -256,9 +278,11 @@ struct Slot {
   int row;            // int4: N index of the block's row (scale lookup)
 };
 
-// How a thread moves its share of one operand tile (ROWS M or N indices x 64 K indices)
-// from HBM to LDS. KIND 0: K-contiguous storage. KIND 1: contiguous along M/N (the
-// operand is transposed in registers). KIND 2: int4 codes packed along K.
+// How a thread moves its share of one operand tile (ROWS M or N indices x one K step of
+// 128 bytes per row: BK = 64 16-bit or 128 fp8 K indices) from HBM to LDS. KIND 0:
+// K-contiguous storage. KIND 1: 16-bit values contiguous along M/N (the operand is
+// transposed in registers). KIND 2: int4 codes packed along K. KIND 3: fp8 values
+// contiguous along M/N (transposed in registers at byte granularity).
 //   KIND 0, block q, vector j: row j*ROWS/4 + q/8, 16-byte chunk q%8 of the step. Eight
 //     consecutive lanes cover one 128-byte row segment: whole lines in HBM, one LDS row.
 //   KIND 1, block q: kh = q%2, v = (q/2) % (ROWS/8), kg = (q/2) / (ROWS/8); vector j is K
@@ -270,27 +294,40 @@ struct Slot {
 //     eight consecutive LDS rows (eight 16-byte bank groups) times two 8-byte halves.
 //   KIND 2, block q: row q/2, K half q%2 (32 codes, 16 bytes) -> four 16-byte stores of
 //     eight binary16 weights each.
-template <int KIND, int ROWS, int THREADS, RowPerm P>
+//   KIND 3, block q: v = q % (ROWS/16), kg = q / (ROWS/16); vector j is K row 4kg + j of
+//     elements 16v..16v+15. After the byte transpose, element e's four K values (one
+//     dword) go to LDS row inv(16v + e) at byte 4kg. With the 256-row, stride-16
+//     permutation, inv(16v + e) = 16e + v: the 16 v of one store instruction land in 16
+//     rows whose 144-byte pitch puts them on 16 different 16-byte bank groups, and the
+//     four kg of the wave fill the four dwords of each group (64 different banks).
+template <int KIND, int ROWS, int THREADS, RowPerm P, int EB = 2>
 struct Operand {
-  static constexpr int BK = 64;
+  static constexpr int BK = 128 / EB;
   static constexpr int PITCH_B = 144;                // LDS row pitch: 128 B data + 16 B pad
   static constexpr int VPB = KIND == 2 ? 1 : 4;
   static constexpr int BLOCKS = ROWS * 2;            // blocks per K step
   static constexpr int SLOTS = (BLOCKS + THREADS - 1) / THREADS;
   static constexpr bool PARTIAL = BLOCKS % THREADS != 0;
-  // LDS-row step between the rows of one transposed vector: inv(8v + e) = inv(8v) + e*ES.
+  // Elements per 16-byte vector along M/N of a transposed operand.
+  static constexpr int VL = KIND == 3 ? 16 : 8;
+  // LDS-row step between the rows of one transposed vector: inv(VL*v + e) = inv(VL*v) + e*ES.
   static constexpr int ES = P.block == 1 ? 1 : P.block / P.stride;
   static constexpr bool es_ok() {
-    for (int v = 0; v < ROWS / 8; ++v)
-      for (int e = 0; e < 8; ++e)
-        if (P.inv(8 * v + e) != P.inv(8 * v) + e * ES) return false;
+    for (int v = 0; v < ROWS / VL; ++v)
+      for (int e = 0; e < VL; ++e)
+        if (P.inv(VL * v + e) != P.inv(VL * v) + e * ES) return false;
     return true;
   }
   static_assert(es_ok(), "row permutation must step evenly inside a vector");
-  static_assert(ROWS % 64 == 0, "tile rows must be whole permutation blocks");
+  static_assert(ROWS % 64 == 0 && ROWS % P.block == 0, "tile rows must be whole permutation blocks");
+  static_assert((KIND != 1 && KIND != 2) || EB == 2, "16-bit operand kinds");
+  static_assert(KIND != 3 || EB == 1, "fp8 operand kind");
+  static_assert(!(PARTIAL && KIND == 2), "int4 blocks must fill every thread");
 
   // Block q of this K split: offsets, K offset and LDS base. Blocks past BLOCKS (idle
-  // lanes of a partial slot) read nothing and store into their own dead row.
+  // lanes of a partial slot) read nothing (zeros) and store them into padding bytes of
+  // their own tile: byte 128 of a row is its pad, and every store offset of a block is a
+  // multiple of the row pitch plus at most the pad's 16 bytes.
   __device__ __forceinline__ static void setup(Slot<VPB>& s, int q, int row0, int rows_total,
                                                int ld, int kb, int K, bool tiled = false) {
     const bool live = q < BLOCKS;
@@ -299,9 +336,9 @@ struct Operand {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = j * (ROWS / 4) + q / 8;
-        s.off[j] = (live && row0 + r < rows_total) ? (uint32_t)((row0 + r) * ld + kb + 8 * c) * 2u : kOOB;
+        s.off[j] = (live && row0 + r < rows_total) ? (uint32_t)((row0 + r) * ld + kb) * EB + 16u * c : kOOB;
       }
-      s.kofs = 8 * c;
+      s.kofs = 16 * c / EB;
       s.wbase = P.inv(q / 8) * PITCH_B + 16 * c;
     } else if constexpr (KIND == 1) {
       const int kh = q % 2, v = (q / 2) % (ROWS / 8), kg = (q / 2) / (ROWS / 8);
@@ -311,6 +348,14 @@ struct Operand {
         s.off[j] = ok ? (uint32_t)((kb + 8 * kg + 4 * kh + j) * ld + row0 + 8 * v) * 2u : kOOB;
       s.kofs = 8 * kg + 4 * kh;
       s.wbase = P.inv(8 * v) * PITCH_B + 16 * kg + 8 * kh;
+    } else if constexpr (KIND == 3) {
+      const int v = q % (ROWS / 16), kg = q / (ROWS / 16);
+      const bool ok = live && row0 + 16 * v < rows_total;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        s.off[j] = ok ? (uint32_t)((kb + 4 * kg + j) * ld + row0 + 16 * v) : kOOB;
+      s.kofs = 4 * kg;
+      s.wbase = P.inv(16 * v) * PITCH_B + 4 * kg;
     } else {
       const int r = q / 2, h = q % 2;
       // column-major packing: byte n*(K/2) + k/2; pre-tiled: 4 KiB blocks of 64 columns x
@@ -323,7 +368,7 @@ struct Operand {
       s.wbase = P.inv(r) * PITCH_B + 64 * h;
       s.row = row0 + r;
     }
-    if (!live) s.wbase = ROWS * PITCH_B - 16;  // last pad bytes of the tile (never read)
+    if (!live) s.wbase = 128;  // row 0's pad (KIND 0: rows j*ROWS/4, KIND 1/3: rows e*ES)
   }
 };
 
@@ -333,7 +378,8 @@ struct Operand {
 // 128 bytes (64 K values) without padding; the 16-byte chunk c of row r is kept in slot
 // c ^ swz(r), swz(r) = (r >> 1) & 7 (a chunk permutation of the K-contiguous layout), so
 // that a fragment read (lanes on 32 consecutive rows, one chunk each) touches every bank
-// group once per 16 lanes. One load instruction of a wave fills eight whole LDS rows
+// group once per 16 lanes (the row is 64 16-bit or 128 fp8 K values; the chunks are the
+// same 16-byte units). One load instruction of a wave fills eight whole LDS rows
 // (1 KiB): lane t writes row t/8, slot t%8, and therefore loads chunk (t%8) ^ swz(row) of
 // that row, so the eight lanes of a row still read one whole 128-byte line.
 __device__ __forceinline__ constexpr int dtl_swz(int r) { return (r >> 1) & 7; }
@@ -350,7 +396,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p);
 }
 
-template <int ROWS, int THREADS>
+template <int ROWS, int THREADS, int EB = 2>
 struct DtlOperand {
   static constexpr int WAVES = THREADS / 64;
   static constexpr int NI = ROWS / (8 * WAVES);  // load instructions per wave and K step
@@ -364,8 +410,8 @@ struct DtlOperand {
     for (int j = 0; j < NI; ++j) {
       const int r = 8 * (wave * NI + j) + lane / 8;
       const int c = (lane & 7) ^ dtl_swz(r);
-      off[j] = row0 + r < rows_total ? (uint32_t)((row0 + r) * ld + 8 * c) * 2u + (uint32_t)kb * 2u : kOOB;
-      kofs[j] = 8 * c;
+      off[j] = row0 + r < rows_total ? (uint32_t)((row0 + r) * ld + kb) * EB + 16u * c : kOOB;
+      kofs[j] = 16 * c / EB;
     }
   }
   // Loads of one K step (byte step d from the split's first step; lim = K indices left)
@@ -465,7 +511,9 @@ __device__ __forceinline__ u32x4 tr_fragment(const char* p) {
 template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN,
           bool PERM, int DTL>
 struct TileCfg {
-  static constexpr int BK = 64;
+  static constexpr int EB = elem_bytes<T>();
+  static constexpr bool F8 = EB == 1;
+  static constexpr int BK = 128 / EB;                    // K per step: 128-byte LDS rows
   static constexpr int THREADS = WM * WN * 64;
   static constexpr int WT_M = MT_M / WM, WT_N = MT_N / WN;
   static constexpr int TM = WT_M / 32, TN = WT_N / 32;   // 32x32 blocks per wave
@@ -476,13 +524,17 @@ struct TileCfg {
   static constexpr bool B_DTL = DTL >= 1 && B_KC && !U4B;
   static constexpr bool A_TR = DTL == 2 && !A_KC;
   static constexpr bool B_TR = DTL == 2 && !B_KC && !U4B;
+  static_assert(!(F8 && (DTL == 2 || U4B)), "fp8: no transposing LDS reads, no int4 B");
   static constexpr bool ANY_DTL = A_DTL || B_DTL || A_TR || B_TR;
-  static constexpr RowPerm PA = (!A_KC && PERM && !A_TR) ? RowPerm{64, 8} : RowPerm{1, 1};
-  static constexpr RowPerm PB = (!B_KC && !U4B && PERM && !B_TR) ? RowPerm{64, 8} : RowPerm{1, 1};
-  using OpA = Operand<A_KC ? 0 : 1, MT_M, THREADS, PA>;
-  using OpB = Operand<U4B ? 2 : (B_KC ? 0 : 1), MT_N, THREADS, PB>;
-  using DA = DtlOperand<MT_M, THREADS>;
-  using DB = DtlOperand<MT_N, THREADS>;
+  // LDS row permutation of an operand transposed in registers (see Operand).
+  static constexpr RowPerm PT = F8 ? RowPerm{256, 16} : RowPerm{64, 8};
+  static constexpr RowPerm PA = (!A_KC && PERM && !A_TR) ? PT : RowPerm{1, 1};
+  static constexpr RowPerm PB = (!B_KC && !U4B && PERM && !B_TR) ? PT : RowPerm{1, 1};
+  static constexpr int KT = F8 ? 3 : 1;                  // kind of a transposed operand
+  using OpA = Operand<A_KC ? 0 : KT, MT_M, THREADS, PA, EB>;
+  using OpB = Operand<U4B ? 2 : (B_KC ? 0 : KT), MT_N, THREADS, PB, EB>;
+  using DA = DtlOperand<MT_M, THREADS, EB>;
+  using DB = DtlOperand<MT_N, THREADS, EB>;
   using TA = DtlTrOperand<A_TR ? MT_M : 256, THREADS>;
   using TB = DtlTrOperand<B_TR ? MT_N : 256, THREADS>;
   // Register-staged load slots per thread (none for a direct-to-LDS operand).
@@ -516,17 +568,41 @@ __device__ __forceinline__ f32x16 mfma32x32x16<BF16T>(u32x4 a, u32x4 b, f32x16 c
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// v_mfma_f32_32x32x64_f8f6f4 with both operands fp8 E4M3 (format code 0) and no block
+// scales: a lane's fragment is 32 bytes, given here as two 16-byte halves.
+__device__ __forceinline__ f32x16 mfma32x32x64_f8(const u32x4 (&a)[2], const u32x4 (&b)[2],
+                                                  f32x16 c) {
+  typedef int v8i32 __attribute__((ext_vector_type(8)));
+  const v8i32 av = {(int)a[0][0], (int)a[0][1], (int)a[0][2], (int)a[0][3],
+                    (int)a[1][0], (int)a[1][1], (int)a[1][2], (int)a[1][3]};
+  const v8i32 bv = {(int)b[0][0], (int)b[0][1], (int)b[0][2], (int)b[0][3],
+                    (int)b[1][0], (int)b[1][1], (int)b[1][2], (int)b[1][3]};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
+}
+
 template <int N> using IC = std::integral_constant<int, N>;
 
 // The epilogue's vector stores for a permuted B: within every wave's 32-row blocks, LDS rows
 // I + 8g (I = 32j + 4h + e, g = 0..3) map to four consecutive logical columns.
-template <RowPerm P, int WT_N>
+template <RowPerm P, int MT_N>
 constexpr bool epilogue_cols_ok() {
   if (P.block == 1) return true;
-  for (int base = 0; base < 4 * WT_N; base += 32)
+  for (int base = 0; base < MT_N; base += 32)
     for (int o = 0; o < 8; ++o)
       for (int g = 1; g < 4; ++g)
         if (P.fwd(base + o + 8 * g) != P.fwd(base + o) + g) return false;
+  return true;
+}
+// The same for 64-column wave tiles whose LDS rows I + 16t (t = 0..3, I = 64w + o,
+// o < 16) map to four consecutive logical columns (the fp8 transposed-operand permutation):
+// a lane's values of blocks j = 0, 1 and groups g, g + 2 form one run.
+template <RowPerm P, int MT_N, int WT_N>
+constexpr bool epilogue_runs16_ok() {
+  if (P.block == 1 || WT_N != 64) return false;
+  for (int base = 0; base < MT_N; base += 64)
+    for (int o = 0; o < 16; ++o)
+      for (int t = 1; t < 4; ++t)
+        if (P.fwd(base + o + 16 * t) != P.fwd(base + o) + t) return false;
   return true;
 }
 
@@ -542,6 +618,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   constexpr int SA = Cfg::SA, SB = Cfg::SB;
   constexpr int SA1 = SA > 0 ? SA : 1, SB1 = SB > 0 ? SB : 1;  // array extents
   static_assert(!(PP && Cfg::ANY_DTL), "the ping-pong schedule stores every operand itself");
+  static_assert(!(PP && Cfg::F8), "the ping-pong schedule is written for 16-bit operands");
+  constexpr int EB = Cfg::EB;
   constexpr RowPerm PA = Cfg::PA, PB = Cfg::PB;
   __shared__ __attribute__((aligned(16))) u32x4 lds[Cfg::LDS_BYTES / 16];
   char* const ldsb = reinterpret_cast<char*>(lds);
@@ -589,8 +667,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
 #pragma unroll
   for (int i = 0; i < SB; ++i) OpB::setup(sb[i], i * THREADS + tid, n0, a.N, a.ldB, kb, a.K, a.b_tiled != 0);
   // Byte step of the offsets per K step.
-  const uint32_t dA = A_KC ? BK * 2u : (uint32_t)(BK * a.ldA) * 2u;
-  const uint32_t dB = U4B ? BK / 2u : (B_KC ? BK * 2u : (uint32_t)(BK * a.ldB) * 2u);
+  const uint32_t dA = A_KC ? BK * EB : (uint32_t)(BK * a.ldA) * EB;
+  const uint32_t dB = U4B ? BK / 2u : (B_KC ? BK * EB : (uint32_t)(BK * a.ldB) * EB);
 
   // Register sets: with two, set (j % 2) holds the global data of K step j between its
   // loads (issued two steps ahead) and its LDS stores (one step ahead); with one, step j's
@@ -653,6 +731,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     for (int i = 0; i < SA; ++i) {
       if constexpr (A_KC) {
         *reinterpret_cast<u32x4*>(sA + sa[i].wbase + P * (MT_M / 4) * 144) = ra[SET][i][P];
+      } else if constexpr (Cfg::F8) {
+        // elements 4P..4P+3 of the block's 16-byte vectors
+        uint32_t o[4];
+        transpose_bytes4(ra[SET][i][0][P], ra[SET][i][1][P], ra[SET][i][2][P], ra[SET][i][3][P], o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          *reinterpret_cast<uint32_t*>(sA + sa[i].wbase + (4 * P + e) * OpA::ES * 144) = o[e];
       } else {
 #pragma unroll
         for (int e = 2 * P; e < 2 * P + 2; ++e)
@@ -667,6 +752,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
         *reinterpret_cast<u32x4*>(sB + sb[i].wbase + 16 * P) = dequant8(rb[SET][i][0][P], s2);
       } else if constexpr (B_KC) {
         *reinterpret_cast<u32x4*>(sB + sb[i].wbase + P * (MT_N / 4) * 144) = rb[SET][i][P];
+      } else if constexpr (Cfg::F8) {
+        uint32_t o[4];
+        transpose_bytes4(rb[SET][i][0][P], rb[SET][i][1][P], rb[SET][i][2][P], rb[SET][i][3][P], o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          *reinterpret_cast<uint32_t*>(sB + sb[i].wbase + (4 * P + e) * OpB::ES * 144) = o[e];
       } else {
 #pragma unroll
         for (int e = 2 * P; e < 2 * P + 2; ++e)
@@ -700,7 +791,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   // Instruction counts of one sub-step, for the interleaving below.
   constexpr int N_MFMA = TM * TN;
   constexpr int N_READ = TM + TN;
-  constexpr int N_WRITE = SA * (A_KC ? 1 : 2) + SB * (U4B ? 1 : (B_KC ? 1 : 2));
+  constexpr int TW = Cfg::F8 ? 4 : 2;   // LDS stores per part of a transposed block
+  constexpr int N_WRITE = SA * (A_KC ? 1 : TW) + SB * (U4B ? 1 : (B_KC ? 1 : TW));
   constexpr int N_VMEM = SA + SB * (U4B ? 2 : 1);
 
   // K step s from LDS buffer CUR (= s % 2), four 16-K sub-steps kk. Sub-step kk also
@@ -787,6 +879,99 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     __syncthreads();
   };
 
+  // fp8 K step s (128 K): two 64-K halves h, one v_mfma_f32_32x32x64 per 32x32 block and
+  // half. A lane's 32-byte fragment of half h is its row's 16-byte chunks 4h + kh and
+  // 4h + 2 + kh (the chunks the 16-bit sub-steps 2h and 2h + 1 read): A and B take the
+  // same chunks, so both put the same K index in the same fragment byte and the products
+  // pair up exactly whatever K order the instruction uses inside the fragment.
+  // One register set per fragment (as many registers as the 16-bit double-buffered
+  // sub-steps): half 0 walks the blocks in a snake, column 0 down then column 1 up, so
+  // B fragment 0 and then the A fragments TM-1 .. 0 and B fragment 1 fall free one by one
+  // and are reloaded with half 1's chunks right there; half 1 walks column 0 up, then
+  // column 1 down, using them in the order they were reloaded (three or more multiplies
+  // after each reload). Loads and stores of the next steps are spread over both halves.
+  auto step8 = [&](int s, auto CUR_, auto LOAD_, auto STORE_) {
+    constexpr int CUR = decltype(CUR_)::value;
+    constexpr bool LOAD = decltype(LOAD_)::value, STORE = decltype(STORE_)::value;
+    static_assert(NS == 2, "fp8 steps keep loads two steps ahead");
+    static_assert(TN == 2, "the snake order is written for two B blocks per wave");
+    const u32x4* st = lds + CUR * Cfg::STAGE16;
+    u32x4 fa[TM][2], fb[TN][2];
+    auto read_a = [&](int i, auto H_) {
+      constexpr int H = decltype(H_)::value;
+      fa[i][0] = st[a_rd[2 * H] + i * 32 * PA16];
+      fa[i][1] = st[a_rd[2 * H + 1] + i * 32 * PA16];
+    };
+    auto read_b = [&](int j, auto H_) {
+      constexpr int H = decltype(H_)::value;
+      fb[j][0] = st[b_rd[2 * H] + j * 32 * PB16];
+      fb[j][1] = st[b_rd[2 * H + 1] + j * 32 * PB16];
+    };
+    auto mma = [&](int i, int j) { acc[i * TN + j] = mfma32x32x64_f8(fb[j], fa[i], acc[i * TN + j]); };
+    // Slot g of a half: one multiply, then that slot's share of the stores and loads.
+    auto slots = [&](auto H_) {
+      constexpr int H = decltype(H_)::value;
+#pragma unroll
+      for (int g = 0; g < N_MFMA; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                            // MFMA
+        // half 0: reloads after the last use of B 0 (slot TM-1), of A TM-1..0 (slots
+        // TM..2TM-1) and of B 1 (slot 2TM-1)
+        if (H == 0 && g >= TM - 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+        if (H == 0 && g == N_MFMA - 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int t = 0; t < (2 * N_WRITE) / N_MFMA + (g < (2 * N_WRITE) % N_MFMA ? 1 : 0); ++t)
+          if (STORE) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);               // DS write
+#pragma unroll
+        for (int t = 0; t < (2 * N_VMEM) / N_MFMA + (g < (2 * N_VMEM) % N_MFMA ? 1 : 0); ++t)
+          if (LOAD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                // VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                            // VALU
+      }
+    };
+    read_b(0, IC<0>{});
+#pragma unroll
+    for (int i = 0; i < TM; ++i) read_a(i, IC<0>{});
+    read_b(1, IC<0>{});
+    if constexpr (Cfg::ANY_DTL) {
+      dtl(s + 1, IC<CUR ^ 1>{});
+      load_part(CUR_, s + 2, IC<0>{}, IC<4>{});
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // half 0
+    if constexpr (LOAD) load_part(CUR_, s + 2, IC<0>{}, IC<2>{});
+    if constexpr (STORE) {
+      store_part(IC<CUR ^ 1>{}, IC<CUR ^ 1>{}, IC<0>{});
+      store_part(IC<CUR ^ 1>{}, IC<CUR ^ 1>{}, IC<1>{});
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) mma(i, 0);
+    read_b(0, IC<1>{});
+#pragma unroll
+    for (int i = TM - 1; i >= 0; --i) {
+      mma(i, 1);
+      read_a(i, IC<1>{});
+    }
+    read_b(1, IC<1>{});
+    slots(IC<0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    // half 1
+    if constexpr (LOAD) load_part(CUR_, s + 2, IC<2>{}, IC<4>{});
+    if constexpr (STORE) {
+      store_part(IC<CUR ^ 1>{}, IC<CUR ^ 1>{}, IC<2>{});
+      store_part(IC<CUR ^ 1>{}, IC<CUR ^ 1>{}, IC<3>{});
+    }
+#pragma unroll
+    for (int i = TM - 1; i >= 0; --i) mma(i, 0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) mma(i, 1);
+    slots(IC<1>{});
+    if constexpr (Cfg::ANY_DTL) __builtin_amdgcn_s_waitcnt(0);  // every load of the step
+    __syncthreads();
+  };
+  auto run_step = [&](int s, auto CUR_, auto LOAD_, auto STORE_) {
+    if constexpr (Cfg::F8) step8(s, CUR_, LOAD_, STORE_);
+    else step(s, CUR_, LOAD_, STORE_);
+  };
+
   using TRUE = std::integral_constant<bool, true>;
   if constexpr (!PP) {
     // Every step loads two ahead and stores one ahead; loads past the split's end use
@@ -806,8 +991,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     __syncthreads();
     using LOADS = std::integral_constant<bool, !Cfg::ANY_DTL>;  // else issued at step start
     for (int s = 0; s < nt; s += 2) {
-      step(s, IC<0>{}, LOADS{}, TRUE{});
-      step(s + 1, IC<1>{}, LOADS{}, TRUE{});
+      run_step(s, IC<0>{}, LOADS{}, TRUE{});
+      run_step(s + 1, IC<1>{}, LOADS{}, TRUE{});
     }
   } else {
     // Ping-pong schedule. The waves form two groups (wave rows wm = 0 and 1, one wave of
@@ -904,7 +1089,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   // for g = 0..3, the four logical columns fwd_B(LDS rows 32j + 8g + 4(l/32) + 0..3).
   // The C tile is staged in LDS by A's LDS row (consecutive lanes on consecutive rows, so
   // the stores spread over the banks) and each staged row goes to global row fwd_A(row).
-  static_assert(epilogue_cols_ok<PB, Cfg::WT_N>(), "permuted B rows must give runs of four columns");
+  constexpr bool COLS4 = epilogue_cols_ok<PB, MT_N>();
+  constexpr bool RUNS16 = !COLS4 && epilogue_runs16_ok<PB, MT_N, Cfg::WT_N>();
   auto epilogue = [&](auto dt_tag) {
     constexpr int DT = decltype(dt_tag)::value;
     using O = typename OutT<DT>::type;
@@ -936,17 +1122,37 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
               o4 w = {cvt_out<DT>(v[4 * g]), cvt_out<DT>(v[4 * g + 1]), cvt_out<DT>(v[4 * g + 2]),
                       cvt_out<DT>(v[4 * g + 3])};
               *reinterpret_cast<o4*>(dst) = w;
-            } else if (g == 0) {
-              // B's rows are permuted: LDS rows nb + e + 8g (g = 0..3) hold the four
-              // consecutive logical columns fwd_B(nb + e) + g, so each e is one vector store.
-              typedef O o4 __attribute__((ext_vector_type(4)));
+            } else if constexpr (COLS4) {
+              if (g == 0) {
+                // B's rows are permuted: LDS rows nb + e + 8g (g = 0..3) hold the four
+                // consecutive logical columns fwd_B(nb + e) + g: one vector store per e.
+                typedef O o4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                O* dst = reinterpret_cast<O*>(cl + (m - lo) * CP + PB.fwd(nb + e) * OB);
-                o4 w = {cvt_out<DT>(v[e]), cvt_out<DT>(v[4 + e]), cvt_out<DT>(v[8 + e]),
-                        cvt_out<DT>(v[12 + e])};
-                *reinterpret_cast<o4*>(dst) = w;
+                for (int e = 0; e < 4; ++e) {
+                  O* dst = reinterpret_cast<O*>(cl + (m - lo) * CP + PB.fwd(nb + e) * OB);
+                  o4 w = {cvt_out<DT>(v[e]), cvt_out<DT>(v[4 + e]), cvt_out<DT>(v[8 + e]),
+                          cvt_out<DT>(v[12 + e])};
+                  *reinterpret_cast<o4*>(dst) = w;
+                }
               }
+            } else if constexpr (RUNS16) {
+              if (j == 0 && g < 2) {
+                // LDS rows nb + e + 16t, t = 2j' + g' (block j', group g + 2g'), hold the
+                // logical columns fwd_B(nb + e) + t: one vector store per e.
+                const f32x16& v1 = acc[i * TN + 1];
+                typedef O o4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  O* dst = reinterpret_cast<O*>(cl + (m - lo) * CP + PB.fwd(nb + e) * OB);
+                  o4 w = {cvt_out<DT>(v[4 * g + e]), cvt_out<DT>(v[4 * g + 8 + e]),
+                          cvt_out<DT>(v1[4 * g + e]), cvt_out<DT>(v1[4 * g + 8 + e])};
+                  *reinterpret_cast<o4*>(dst) = w;
+                }
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                *reinterpret_cast<O*>(cl + (m - lo) * CP + PB.fwd(nb + e) * OB) = cvt_out<DT>(v[4 * g + e]);
             }
           }
         }
@@ -1175,7 +1381,9 @@ hipError_t launch_skinny(const Plan& p, const KArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <class T> constexpr int dt_code() { return std::is_same<T, F16T>::value ? DT_F16 : DT_BF16; }
+template <class T> constexpr int dt_code() {
+  return std::is_same<T, F16T>::value ? DT_F16 : (std::is_same<T, F8T>::value ? DT_F8 : DT_BF16);
+}
 
 struct Variant {
   VariantInfo info;
@@ -1184,7 +1392,8 @@ struct Variant {
 
 #define TILE_X(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, PP, DTL)                            \
   Variant{VariantInfo{KERNEL_TILE, dt_code<T>(), (U4) ? DT_U4 : dt_code<T>(), (AKC) ? 0 : 1,  \
-                      (BKC) ? 1 : 0, MTM, MTN, 64, (WM) * (WN), 1, PERM,                     \
+                      (BKC) ? 1 : 0, MTM, MTN,                                               \
+                      TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::BK, (WM) * (WN), 1, PERM, \
                       TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::LDS_BYTES,      \
                       TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::NSETS, 1, PP,   \
                       (TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::A_DTL ? 1 : 0) | \
@@ -1231,6 +1440,7 @@ struct Variant {
 // Instantiation tables, one per translation unit.
 int variants_f16(const Variant** out);
 int variants_bf16(const Variant** out);
+int variants_f8(const Variant** out);
 int variants_misc(const Variant** out);
 
 }  // namespace dg

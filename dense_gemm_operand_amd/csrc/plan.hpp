@@ -7,7 +7,7 @@ namespace dg {
 enum Kernel : int32_t { KERNEL_TILE = 0, KERNEL_SKINNY = 1 };
 
 // Element-type codes (same numbering as the public header).
-enum Dtype : int32_t { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_U4 = 3 };
+enum Dtype : int32_t { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_U4 = 3, DT_F8 = 4 };
 
 struct Plan {
   int64_t M = 0, N = 0, K = 0;
@@ -49,7 +49,7 @@ struct RunArgs {
 // Instantiation table of the launcher (kernels.hip).
 struct VariantInfo {
   int32_t kernel;
-  int32_t dtype_a, dtype_b;       // DT_F16/DT_BF16; dtype_b DT_U4 for int4
+  int32_t dtype_a, dtype_b;       // DT_F16/DT_BF16/DT_F8; dtype_b DT_U4 for int4
   int32_t layout_a, layout_b;     // required layouts
   int32_t tile_m, tile_n, tile_k;
   int32_t waves;

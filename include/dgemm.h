@@ -42,8 +42,11 @@ extern "C" {
  * gemm_pack_u4_tiled() converts from the column-major packing. Needs N % 64 == 0. */
 enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1, GEMM_U4_TILED = 2 };
 
-/* Element types. GEMM_U4 is valid for B only: two 4-bit codes per byte along K. */
-enum { GEMM_F32 = 0, GEMM_F16 = 1, GEMM_BF16 = 2, GEMM_U4 = 3 };
+/* Element types. GEMM_U4 is valid for B only: two 4-bit codes per byte along K.
+ * GEMM_F8 is the 8-bit OCP E4M3 format (sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * no infinities; S.1111.111 is NaN; largest finite magnitude 448), valid for A and B
+ * together, one byte per element. */
+enum { GEMM_F32 = 0, GEMM_F16 = 1, GEMM_BF16 = 2, GEMM_U4 = 3, GEMM_F8 = 4 };
 
 /* Status codes. */
 enum {
@@ -102,16 +105,21 @@ typedef struct {
 /* Make a plan for C (M x N, row-major, dtype_c) = A (M x K) * B (K x N).
  *
  * layout_a/layout_b: GEMM_ROW_MAJOR or GEMM_COL_MAJOR storage of the logical operands.
- * dtype_a: GEMM_F16 or GEMM_BF16. dtype_b: the same as dtype_a, or GEMM_U4 with
+ * dtype_a: GEMM_F16, GEMM_BF16 or GEMM_F8. dtype_b: the same as dtype_a, or GEMM_U4 with
  *   dtype_a == GEMM_F16, layout_b == GEMM_COL_MAJOR (codes packed along K) or
  *   GEMM_U4_TILED, and a non-null `quant` (otherwise quant must be NULL or is ignored).
+ *   fp8 operands are multiplied exactly and summed in fp32 by the matrix cores
+ *   (v_mfma_f32_32x32x64_f8f6f4, no block scales) on 256x256 tiles with a K step of 128;
+ *   a transposed fp8 operand is transposed in registers at byte granularity and its LDS
+ *   rows are permuted with perm_block = 256, perm_stride = 16.
  * dtype_c: GEMM_F32, GEMM_F16 or GEMM_BF16 (round-to-nearest-even from fp32 sums).
  * split_k: 0 lets the planner choose (waste-ratio search over the workgroup slots,
  *   i.e. CU count times resident workgroups per CU, BitBLAS PR 268 "SplitK Infer",
  *   capped at 16); otherwise 1, 2, 4, 8 or 16.
- * Constraints: M, N, K >= 1; the contiguous extent of each operand is a multiple of 8
- *   elements (K for row-major A and column-major B, M for column-major A, N for
- *   row-major B); int4 needs K % 128 == 0. Violations give GEMM_ERR_UNSUPPORTED.
+ * Constraints: M, N, K >= 1; the contiguous extent of each operand is a multiple of 16
+ *   bytes, i.e. 8 16-bit or 16 fp8 elements (K for row-major A and column-major B, M for
+ *   column-major A, N for row-major B); int4 needs K % 128 == 0. Violations give
+ *   GEMM_ERR_UNSUPPORTED.
  * The plan binds to the HIP device current at this call (its CU count feeds the
  * split-K search; the environment variable DGEMM_FAKE_CU_COUNT replaces the query so
  * that planning works without a device). Host only: no allocation, no launch.

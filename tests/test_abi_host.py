@@ -246,3 +246,42 @@ def test_tiled_int4_plans(fake_cus):
         i = dg.gemm_plan_query(p)
         dg.gemm_plan_destroy(p)
         assert i["layout_b"] == T and i["kernel"] == (1 if M == 16 else 0)
+
+
+F8 = dg.GEMM_F8
+
+
+def test_fp8_plans(fake_cus):
+    # every layout pair plans onto a 256x256 tile with a 128-K step; the transposed operand
+    # gets the fp8 row permutation (256 rows, stride 16) and K-contiguous ones go straight
+    # to LDS
+    want_dtl = {(ROW, COL): 3, (COL, COL): 2, (ROW, ROW): 1, (COL, ROW): 0}
+    for (la, lb), bits in want_dtl.items():
+        p = dg.gemm_plan(4096, 4096, 4096, la, lb, F8, F8, F16, 0)
+        i = dg.gemm_plan_query(p)
+        dg.gemm_plan_destroy(p)
+        assert (i["tile_m"], i["tile_n"], i["tile_k"], i["waves"], i["split_k"]) == (256, 256, 128, 8, 1)
+        assert i["direct_lds"] == bits
+        assert (i["perm_block"], i["perm_stride"]) == ((1, 1) if bits == 3 else (256, 16))
+        assert i["lds_bytes"] <= 160 * 1024
+    # contiguous extents in multiples of 16 bytes: 16 fp8 elements (8 are enough for fp16)
+    assert _plan_status(64, 64, 24, ROW, COL, F8, F8, F16, 0)[0] == dg.GEMM_ERR_UNSUPPORTED
+    assert _plan_status(64, 64, 24, ROW, COL, F16, F16, F16, 0)[0] == dg.GEMM_OK
+    assert _plan_status(40, 64, 64, COL, COL, F8, F8, F16, 0)[0] == dg.GEMM_ERR_UNSUPPORTED
+    assert _plan_status(64, 40, 64, ROW, ROW, F8, F8, F16, 0)[0] == dg.GEMM_ERR_UNSUPPORTED
+    # K of two transposed operands is free; M <= 16 uses the tiled kernel
+    assert _plan_status(48, 48, 37, COL, ROW, F8, F8, F32, 0)[0] == dg.GEMM_OK
+    p = dg.gemm_plan(16, 8192, 4096, ROW, COL, F8, F8, F16, 0)
+    i = dg.gemm_plan_query(p)
+    dg.gemm_plan_destroy(p)
+    assert i["kernel"] == 0 and i["tile_k"] == 128
+    # fp8 output, mixed operand types and fp8 with int4 are not offered
+    assert _plan_status(64, 64, 64, ROW, COL, F8, F8, F8, 0)[0] == dg.GEMM_ERR_UNSUPPORTED
+    assert _plan_status(64, 64, 64, ROW, COL, F8, F16, F16, 0)[0] == dg.GEMM_ERR_UNSUPPORTED
+    assert _plan_status(64, 64, 64, ROW, COL, F16, F8, F16, 0)[0] == dg.GEMM_ERR_UNSUPPORTED
+    assert _plan_status(64, 64, 256, ROW, COL, F8, U4, F16, 0, quant=dg.int4_quant())[0] == dg.GEMM_ERR_UNSUPPORTED
+    # split-K granule is the 128-K step
+    p = dg.gemm_plan(16, 8192, 28672, ROW, COL, F8, F8, F16, 0)
+    i = dg.gemm_plan_query(p)
+    dg.gemm_plan_destroy(p)
+    assert i["split_k"] == oracle.splitk_factor(16, 8192, 28672, 256, 256, 128, 256)
