@@ -1,4 +1,4 @@
-"""CPU oracle for the non-TN operand GEMM (fp64, plain loops).
+"""CPU oracle for the non-TN operand GEMM and for attention's P*V product (fp64, plain loops).
 
 TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU-baseline leg
 import this package; the product package never does. It shares no code with the HIP
@@ -12,6 +12,9 @@ Contents and the passage each follows:
   * ``dequant_u4``      -- (q - zero) * s rounded once to binary16.
   * ``decode(.., "f8")`` -- 8-bit E4M3 operands (OCP convention: bias 7, no infinity,
                            one NaN pattern per sign), exact in fp64.
+  * ``attention``       -- softmax(scale * Q K^T) V by definition (fp64 scores, exp of the
+                           shifted scores, fp64 sums, one division, one rounding): the
+                           flash-attention second dot named in Triton PR 5223, "Introduction".
   * ``splitk_factor``   -- BitBLAS PR 268, "SplitK Infer" code block, with ceil grid.
   * ``perm_fwd/perm_inv`` -- rocm-libraries PR 2487, "Add support for permuting perpDim",
                            forward and inverse mapping formulas.
@@ -61,8 +64,11 @@ def _L():
         lib.oracle_dequant_u4.argtypes = [vp, vp, i64, i64, i64, ctypes.c_int, dp]
         lib.oracle_gemm_f64.argtypes = [dp, dp, i64, i64, i64, i64, i64, dp]
         lib.oracle_threads.argtypes = []
+        lib.oracle_attention_f64.argtypes = [dp, dp, dp, i64, i64, i64, i64, ctypes.c_double,
+                                             i64, i64, dp]
         for f in (lib.oracle_decode, lib.oracle_encode, lib.oracle_logical,
-                  lib.oracle_dequant_u4, lib.oracle_gemm_f64, lib.oracle_threads):
+                  lib.oracle_dequant_u4, lib.oracle_gemm_f64, lib.oracle_threads,
+                  lib.oracle_attention_f64):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -157,6 +163,34 @@ def gemm(A_bits, B_bits, M: int, N: int, K: int, layout_a: str, layout_b: str,
                   scales_bits, group, zero)
     c64 = gemm_f64(a, b, rows)
     return c64, encode(c64, fmt_c)
+
+
+def attention_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                  rows: tuple[int, int] | None = None) -> np.ndarray:
+    """softmax(scale * q k^T) v per slice for fp64 q [BH, Sq, D], k and v [BH, Sk, D].
+    Returns [BH, Sq, D], or the flattened rows [r0, r1) of (slice, query) as [r1 - r0, D]."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    BH, Sq, D = q.shape
+    assert k.shape[0] == BH and k.shape[2] == D and v.shape == k.shape
+    Sk = k.shape[1]
+    r0, r1 = rows if rows is not None else (0, BH * Sq)
+    o = np.empty((r1 - r0, D), dtype=np.float64)
+    if _L().oracle_attention_f64(_dp(q), _dp(k), _dp(v), BH, Sq, Sk, D, float(scale), r0, r1, _dp(o)):
+        raise ValueError("bad attention arguments")
+    return o.reshape(BH, Sq, D) if rows is None else o
+
+
+def attention(q_bits, k_bits, v_bits, BH: int, Sq: int, Sk: int, D: int, fmt: str,
+              fmt_o: str, scale: float, rows: tuple[int, int] | None = None):
+    """Attention forward by definition from stored bits ([BH][S][D], head dim contiguous).
+    Returns (o64, o_bits): fp64 outputs and their single rounding to ``fmt_o``."""
+    q = decode(np.asarray(q_bits).reshape(-1), fmt).reshape(BH, Sq, D)
+    k = decode(np.asarray(k_bits).reshape(-1), fmt).reshape(BH, Sk, D)
+    v = decode(np.asarray(v_bits).reshape(-1), fmt).reshape(BH, Sk, D)
+    o64 = attention_f64(q, k, v, scale, rows)
+    return o64, encode(o64, fmt_o)
 
 
 def splitk_factor(M: int, N: int, K: int, block_m: int, block_n: int, block_k: int,

@@ -1,5 +1,6 @@
 /*
- * CPU oracle for C = A * B with operands that may be stored row- or column-major.
+ * CPU oracle for C = A * B with operands that may be stored row- or column-major, and for
+ * the attention forward product whose second multiply takes a non-K-contiguous V.
  *
  * TEST INFRASTRUCTURE ONLY. Nothing in the product library calls, links or includes this
  * file; only the tests, the smoke check and the benchmark's CPU-baseline leg load it.
@@ -25,6 +26,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -191,6 +193,50 @@ int oracle_gemm_f64(const double* a, const double* b, int64_t M, int64_t N, int6
       const double* bk = b + k * N;
       for (int64_t j = 0; j < N; ++j) ci[j] += aik * bk[j];
     }
+  }
+  return 0;
+}
+
+/* Attention forward, the product whose second matrix multiply (P times V) takes V as a
+ * non-K-contiguous operand: V is stored [key][head dim], its reduction index (the key) is
+ * the strided one (Triton PR 5223, "Introduction": the second dot operation of flash
+ * attention). Written from the definition of scaled softmax attention, per batch-head
+ * slice h and query row i:
+ *   1. s(j) = scale * sum_d q(i, d) * k(j, d)       for every key j (fp64 dot products);
+ *   2. p(j) = exp(s(j) - max_j s(j))                (the shift cancels in step 3 and keeps
+ *                                                    every exponent <= 0);
+ *   3. o(i, d) = sum_j p(j) * v(j, d) / sum_j p(j)  (fp64 sums, one division).
+ * q is [BH][Sq][D], k and v are [BH][Sk][D], o is [BH][Sq][D], all row-major with the head
+ * dimension contiguous. Rows r = h * Sq + i in [row_begin, row_end) are computed; o holds
+ * them consecutively. exp is the C library's. */
+int oracle_attention_f64(const double* q, const double* k, const double* v, int64_t BH,
+                         int64_t Sq, int64_t Sk, int64_t D, double scale, int64_t row_begin,
+                         int64_t row_end, double* o) {
+  if (row_begin < 0 || row_end > BH * Sq || row_begin > row_end || Sk < 1 || D < 1) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = row_begin; r < row_end; ++r) {
+    const int64_t h = r / Sq;
+    const double* qi = q + r * D;
+    const double* kh = k + h * Sk * D;
+    const double* vh = v + h * Sk * D;
+    double* oi = o + (r - row_begin) * D;
+    double* sj = (double*)malloc((size_t)Sk * sizeof(double));
+    double smax = -INFINITY;
+    for (int64_t j = 0; j < Sk; ++j) {
+      double acc = 0.0;
+      for (int64_t d = 0; d < D; ++d) acc += qi[d] * kh[j * D + d];
+      sj[j] = scale * acc;
+      if (sj[j] > smax) smax = sj[j];
+    }
+    double denom = 0.0;
+    for (int64_t d = 0; d < D; ++d) oi[d] = 0.0;
+    for (int64_t j = 0; j < Sk; ++j) {
+      const double pj = exp(sj[j] - smax);
+      denom += pj;
+      for (int64_t d = 0; d < D; ++d) oi[d] += pj * vh[j * D + d];
+    }
+    for (int64_t d = 0; d < D; ++d) oi[d] /= denom;
+    free(sj);
   }
   return 0;
 }

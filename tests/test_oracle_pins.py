@@ -311,3 +311,94 @@ def test_fp8_gemm_with_integer_entries_is_the_integer_product():
             c64, _ = oracle.gemm(synth.store(a, la), synth.store(b, lb), M, N, K, la, lb,
                                  "f8", "f32")
             assert np.array_equal(c64, (ai @ bi).astype(np.float64))
+
+
+# ---------------------------------------------------------------- attention (P * V)
+
+def _att(q, k, v, scale):
+    return oracle.attention_f64(q[None], k[None], v[None], scale)[0]
+
+
+def test_attention_zero_queries_average_the_values():
+    # q = 0: every score is 0, the weights are uniform, each output row is the mean of V
+    rng = np.random.default_rng(301)
+    Sk, D = 37, 16
+    k = rng.standard_normal((Sk, D))
+    v = rng.standard_normal((Sk, D))
+    o = _att(np.zeros((5, D)), k, v, 0.3)
+    assert np.allclose(o, np.broadcast_to(v.mean(axis=0), o.shape), rtol=0, atol=1e-15)
+
+
+def test_attention_single_key_returns_its_value_exactly():
+    rng = np.random.default_rng(302)
+    q, k, v = rng.standard_normal((4, 8)), rng.standard_normal((1, 8)), rng.standard_normal((1, 8))
+    assert np.array_equal(_att(q, k, v, 2.0), np.broadcast_to(v[0], (4, 8)))
+
+
+def test_attention_two_keys_closed_form():
+    # q = (2, 0, 0), k0 = (1, 0, 0), k1 = (0, 1, 0), scale 0.5: scores 1 and 0, so the
+    # weight of key 0 is the logistic function at 1 = e / (1 + e) = 0.7310585786300049
+    q = np.array([[2.0, 0.0, 0.0]])
+    k = np.array([[1.0, 0.0, 0.0], [0.0, 1.0, 0.0]])
+    v = np.array([[1.0, 10.0, -3.0], [0.0, -2.0, 5.0]])
+    w0 = 0.7310585786300049
+    want = w0 * v[0] + (1.0 - w0) * v[1]
+    assert np.allclose(_att(q, k, v, 0.5)[0], want, rtol=1e-15, atol=1e-15)
+    # swapping the roles of the keys swaps the weights (the query side is not transposed)
+    assert np.allclose(_att(q, k[::-1].copy(), v, 0.5)[0], (1 - w0) * v[0] + w0 * v[1], rtol=1e-15, atol=1e-15)
+
+
+def test_attention_dominant_key_selects_its_value():
+    # one key scores 200 above the others: its weight is 1 to within exp(-200)
+    rng = np.random.default_rng(303)
+    Sk, D = 50, 8
+    k = rng.standard_normal((Sk, D)) * 0.01
+    q = np.zeros((3, D))
+    q[:, 0] = 1.0
+    k[17, 0] = 200.0
+    v = rng.standard_normal((Sk, D))
+    assert np.allclose(_att(q, k, v, 1.0), np.broadcast_to(v[17], (3, D)), rtol=0, atol=1e-12)
+
+
+def test_attention_invariances():
+    rng = np.random.default_rng(304)
+    Sq, Sk, D = 6, 23, 12
+    q, k, v = rng.standard_normal((Sq, D)), rng.standard_normal((Sk, D)), rng.standard_normal((Sk, D))
+    o = _att(q, k, v, 0.7)
+    # a vector added to every key shifts each query's scores by a constant: no change
+    c = rng.standard_normal(D)
+    assert np.allclose(_att(q, k + c, v, 0.7), o, rtol=1e-12, atol=1e-12)
+    # keys and values permuted together: no change; queries permuted: rows permuted
+    pk = rng.permutation(Sk)
+    assert np.allclose(_att(q, k[pk], v[pk], 0.7), o, rtol=1e-12, atol=1e-13)
+    pq = rng.permutation(Sq)
+    assert np.allclose(_att(q[pq], k, v, 0.7), o[pq], rtol=0, atol=1e-15)
+    # the scale multiplies the scores: scale s on q equals scale 1 on s*q
+    assert np.allclose(_att(0.7 * q, k, v, 1.0), o, rtol=1e-12, atol=1e-13)
+    # linear in V, and every output lies in the convex hull of the value rows
+    v2 = rng.standard_normal((Sk, D))
+    assert np.allclose(_att(q, k, 2 * v - 3 * v2, 0.7), 2 * o - 3 * _att(q, k, v2, 0.7), rtol=1e-12, atol=1e-12)
+    assert np.all(o <= v.max(axis=0) + 1e-15) and np.all(o >= v.min(axis=0) - 1e-15)
+
+
+def test_attention_slices_are_independent_and_rows_sample_correctly():
+    rng = np.random.default_rng(305)
+    BH, Sq, Sk, D = 3, 5, 9, 4
+    q, k, v = (rng.standard_normal((BH, Sq, D)), rng.standard_normal((BH, Sk, D)),
+               rng.standard_normal((BH, Sk, D)))
+    o = oracle.attention_f64(q, k, v, 0.5)
+    for h in range(BH):
+        assert np.array_equal(o[h], _att(q[h], k[h], v[h], 0.5))
+    part = oracle.attention_f64(q, k, v, 0.5, rows=(4, 12))
+    assert np.array_equal(part, o.reshape(-1, D)[4:12])
+
+
+def test_attention_from_bits_rounds_once():
+    # fp16 bits in, fp16 bits out: the result is the fp64 value rounded by numpy
+    rng = np.random.default_rng(306)
+    BH, Sq, Sk, D = 2, 4, 7, 8
+    qb = synth.to_bits(rng.standard_normal((BH, Sq, D)), "f16")
+    kb = synth.to_bits(rng.standard_normal((BH, Sk, D)), "f16")
+    vb = synth.to_bits(rng.standard_normal((BH, Sk, D)), "f16")
+    o64, obits = oracle.attention(qb, kb, vb, BH, Sq, Sk, D, "f16", "f16", 0.25)
+    assert np.array_equal(obits.reshape(-1), o64.reshape(-1).astype(np.float16).view(np.uint16))
