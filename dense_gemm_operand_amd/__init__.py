@@ -1,9 +1,9 @@
-"""Python binding of libdgemm (include/dgemm.h): argument marshalling only.
+"""Python binding of libdgemm (include/dgemm.h, include/dattn.h): argument marshalling only.
 
 Every function has the name of the C entry point it wraps. Device buffers are passed as
-torch tensors (or raw integer device pointers); every step of the GEMM runs in the HIP
-kernels of libdgemm.so. There is no fallback: if the library is missing, loading fails
-with an error that says how to build it.
+torch tensors (or raw integer device pointers); every step of the GEMM and of the attention
+forward runs in the HIP kernels of libdgemm.so. There is no fallback: if the library is
+missing, loading fails with an error that says how to build it.
 """
 from __future__ import annotations
 
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_lds_row_perm.restype = i32
         L.gemm_pack_u4_tiled.argtypes = [vp, vp, i64, i64]
         L.gemm_pack_u4_tiled.restype = i32
+        L.attn_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, ctypes.c_float, vp]
+        L.attn_fwd.restype = i32
         _lib = L
     return _lib
 
@@ -151,6 +153,21 @@ def gemm_run(plan: int, A, B, scales, C, workspace=None, stream=None) -> None:
                         _nbytes(workspace), stream)
     if st != GEMM_OK:
         raise GemmError(st, "gemm_run")
+
+
+def attn_fwd(Q, K, V, O, BH: int, Sq: int, Sk: int, D: int, dtype, scale: float,
+             stream=None) -> None:
+    """Enqueue O = softmax(scale * Q K^T) V (include/dattn.h). Q, O: BH x Sq x D, K, V:
+    BH x Sk x D device tensors (or raw pointers), head dim contiguous; dtype "f16"/"bf16"."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    st = lib().attn_fwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), BH, Sq, Sk, D, _code(dtype, DTYPE),
+                        float(scale), stream)
+    if st != GEMM_OK:
+        raise GemmError(st, "attn_fwd")
 
 
 def gemm_plan_query(plan: int) -> dict:

@@ -1,4 +1,5 @@
-"""Build libdgemm.so (HIP kernels for gfx950 + host planner + C ABI) in-tree with hipcc.
+"""Build libdgemm.so (GEMM and attention HIP kernels for gfx950, host planner, C ABI) in-tree
+with hipcc.
 
 Usage: python -m dense_gemm_operand_amd.build  (or call build()).
 """
@@ -21,7 +22,8 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument"]
-SOURCES = ["inst_f16.hip", "inst_bf16.hip", "inst_f8.hip", "inst_misc.hip", "host.cpp"]
+SOURCES = ["inst_f16.hip", "inst_bf16.hip", "inst_f8.hip", "inst_misc.hip", "inst_attn.hip",
+           "host.cpp"]
 
 
 def _compile(src: str) -> str:

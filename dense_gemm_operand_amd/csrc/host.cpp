@@ -5,9 +5,11 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <cmath>
 #include <cstring>
 #include <new>
 
+#include "../../include/dattn.h"
 #include "../../include/dgemm.h"
 #include "lds_layout.hpp"
 #include "plan.hpp"
@@ -369,6 +371,28 @@ const char* gemm_status_string(int status) {
     case GEMM_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
   }
+}
+
+int attn_fwd(const void* Q, const void* K, const void* V, void* O, int64_t BH, int64_t Sq,
+             int64_t Sk, int64_t D, int dtype, float scale, void* stream) {
+  using namespace dg;
+  if (!Q || !K || !V || !O) return GEMM_ERR_INVALID_ARG;
+  if (BH <= 0 || Sq <= 0 || Sk <= 0 || D <= 0) return GEMM_ERR_INVALID_ARG;
+  if (dtype < 0 || dtype > 4 || !std::isfinite(scale)) return GEMM_ERR_INVALID_ARG;
+  if (dtype != DT_F16 && dtype != DT_BF16) return GEMM_ERR_UNSUPPORTED;
+  if (D != 128) return GEMM_ERR_UNSUPPORTED;
+  const int64_t lim = ((int64_t)1 << 31) - 16;
+  if (BH * Sq * D * 2 >= lim || BH * Sk * D * 2 >= lim) return GEMM_ERR_UNSUPPORTED;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return GEMM_ERR_MISALIGNED;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_ERR_NO_DEVICE;
+  const AttnLaunch l{Q, K, V, O, BH, Sq, Sk, D, dtype, scale};
+  const int e = launch_attn(l, stream);
+  if (e != 0) {
+    if (debug_on()) std::fprintf(stderr, "[dgemm] attention launch failed: %s\n", hipGetErrorString((hipError_t)e));
+    return GEMM_ERR_HIP;
+  }
+  return GEMM_OK;
 }
 
 int gemm_lds_row_perm(int block, int stride, int index, int inverse) {

@@ -63,6 +63,19 @@ struct VariantInfo {
                                   // bit 2 A, bit 3 B transposed by the LDS reads
 };
 
+// One attention forward call (validated by the ABI layer).
+struct AttnLaunch {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  int64_t BH, Sq, Sk, D;
+  int32_t dtype;
+  float scale;
+};
+// Returns 0 or a hipError_t value.
+int launch_attn(const AttnLaunch& l, void* stream);
+
 int variant_count();
 const VariantInfo& variant_info(int i);
 // Returns 0 or a hipError_t value.

@@ -14,6 +14,9 @@ fp64 in the order A, B, codes, scales, then converted once to the storage format
                     packed two per byte along K (low nibble = even k), zero point 8,
                     fp16 scales [K/128][N] U[0.005, 0.02]; fp16 C
   square_4096_f8    4096^3 8-bit E4M3 (OCP) operands, BLAS NN storage, N(0, 1), fp16 C
+Attention forward (Q, K, V and O [batch*heads][seq][head dim], head dim contiguous; drawn
+in the order Q, K, V, each N(0, 1), converted once; scale 1/sqrt(head dim)):
+  attn_4096         batch 4 x 16 heads, 4096 queries and keys, head dim 128, fp16
 """
 from __future__ import annotations
 
@@ -59,6 +62,44 @@ WORKLOADS = {
 LAYOUT_LETTERS = {  # BLAS column-major lettering -> (A storage, B storage)
     "NN": ("col", "col"), "NT": ("col", "row"), "TN": ("row", "col"), "TT": ("row", "row"),
 }
+
+
+@dataclass(frozen=True)
+class AttnWorkload:
+    name: str
+    index: int
+    batch: int
+    heads: int
+    seq_q: int
+    seq_k: int
+    head_dim: int
+    dtype: str             # "f16" or "bf16" (Q, K, V and O)
+
+    @property
+    def BH(self) -> int:
+        return self.batch * self.heads
+
+
+ATTN_WORKLOADS = {
+    "attn_4096": AttnWorkload("attn_4096", 6, 4, 16, 4096, 4096, 128, "f16"),
+}
+
+
+def make_attn_inputs(w: AttnWorkload, BH: int | None = None, Sq: int | None = None,
+                     Sk: int | None = None, dtype: str | None = None,
+                     seed: int | None = None) -> dict:
+    """Seeded Q, K, V bits ([BH][S][D], flat) of an attention workload, optionally resized."""
+    BH = w.BH if BH is None else BH
+    Sq = w.seq_q if Sq is None else Sq
+    Sk = w.seq_k if Sk is None else Sk
+    dt = w.dtype if dtype is None else dtype
+    D = w.head_dim
+    rng = np.random.default_rng(1234 + w.index if seed is None else seed)
+    q = to_bits(rng.standard_normal((BH, Sq, D)), dt)
+    k = to_bits(rng.standard_normal((BH, Sk, D)), dt)
+    v = to_bits(rng.standard_normal((BH, Sk, D)), dt)
+    return {"BH": BH, "Sq": Sq, "Sk": Sk, "D": D, "dtype": dt, "scale": 1.0 / np.sqrt(D),
+            "Q": q.reshape(-1), "K": k.reshape(-1), "V": v.reshape(-1)}
 
 
 def to_bits(x: np.ndarray, dtype: str) -> np.ndarray:

@@ -285,3 +285,43 @@ def test_fp8_plans(fake_cus):
     i = dg.gemm_plan_query(p)
     dg.gemm_plan_destroy(p)
     assert i["split_k"] == oracle.splitk_factor(16, 8192, 28672, 256, 256, 128, 256)
+
+
+ATTN_HEADER = os.path.join(ROOT, "include", "dattn.h")
+
+
+def test_attention_header_entry_point_is_exported():
+    text = re.sub(r"/\*.*?\*/", "", open(ATTN_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["attn_fwd"]
+    lib = ctypes.CDLL(dg.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_attention_rejects_bad_arguments_before_any_device_work():
+    L = dg.lib()
+    P = 0x10000   # never dereferenced
+    ok = (P, P + 0x100000, P + 0x200000, P + 0x300000, 2, 256, 256, 128, F16, 0.125, None)
+    cases = [
+        ((None,) + ok[1:], dg.GEMM_ERR_INVALID_ARG),
+        (ok[:3] + (None,) + ok[4:], dg.GEMM_ERR_INVALID_ARG),
+        (ok[:4] + (0,) + ok[5:], dg.GEMM_ERR_INVALID_ARG),
+        (ok[:5] + (-1,) + ok[6:], dg.GEMM_ERR_INVALID_ARG),
+        (ok[:6] + (0,) + ok[7:], dg.GEMM_ERR_INVALID_ARG),
+        (ok[:8] + (9,) + ok[9:], dg.GEMM_ERR_INVALID_ARG),
+        (ok[:9] + (float("nan"),) + ok[10:], dg.GEMM_ERR_INVALID_ARG),
+        (ok[:9] + (float("inf"),) + ok[10:], dg.GEMM_ERR_INVALID_ARG),
+        (ok[:7] + (64,) + ok[8:], dg.GEMM_ERR_UNSUPPORTED),            # head dim
+        (ok[:8] + (dg.GEMM_F32,) + ok[9:], dg.GEMM_ERR_UNSUPPORTED),   # fp32 operands
+        (ok[:8] + (F8,) + ok[9:], dg.GEMM_ERR_UNSUPPORTED),
+        (ok[:4] + (64, 1 << 20) + ok[6:], dg.GEMM_ERR_UNSUPPORTED),    # Q beyond 2 GiB
+        (ok[:4] + (64, 256, 1 << 20) + ok[7:], dg.GEMM_ERR_UNSUPPORTED),
+        ((P + 8,) + ok[1:], dg.GEMM_ERR_MISALIGNED),
+        (ok[:3] + (P + 0x300002,) + ok[4:], dg.GEMM_ERR_MISALIGNED),
+    ]
+    for args, want in cases:
+        assert L.attn_fwd(*args) == want, args
+    import torch
+    if not torch.cuda.is_available():
+        assert L.attn_fwd(*ok) == dg.GEMM_ERR_NO_DEVICE
