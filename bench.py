@@ -9,7 +9,8 @@ Prints one JSON line: the headline TFLOP/s, a roofline object for the GEMM kerne
 HIP events on the launch stream), the CPU oracle's throughput on a bounded sample of
 the same product, and the other workloads (other layouts, the non-power-of-2 bf16
 GEMM, skinny split-K and int4 shapes in GB/s, the fp8 E4M3 4096^3 GEMM against the fp8
-matrix peak) under "workloads".
+matrix peak, and the attention forward whose P*V takes V through the transposing loader)
+under "workloads".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only-headline]
        python bench.py --copy-probe   (plain device copy of known size, for scaling
@@ -158,6 +159,29 @@ class Gemm:
 
     def close(self):
         self.dg.gemm_plan_destroy(self.plan)
+
+
+class Attn:
+    """One attention forward workload with device Q, K, V, O."""
+
+    def __init__(self, w, dtype=None):
+        import torch
+        import dense_gemm_operand_amd as dg
+        from dense_gemm_operand_amd import synth
+        self.dg, self.torch, self.w = dg, torch, w
+        inp = synth.make_attn_inputs(w, dtype=dtype)
+        self.inp = inp
+        dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
+        self.Q, self.K, self.V = dev(inp["Q"]), dev(inp["K"]), dev(inp["V"])
+        self.O = torch.empty_like(self.Q)
+        self.args = (self.Q, self.K, self.V, self.O, inp["BH"], inp["Sq"], inp["Sk"], inp["D"],
+                     inp["dtype"], inp["scale"])
+        self.flops = 4.0 * inp["BH"] * inp["Sq"] * inp["Sk"] * inp["D"]
+
+    def run(self):
+        self.dg.attn_fwd(*self.args)
+
+    time_events = Gemm.time_events
 
 
 def cpu_baseline(g: Gemm, budget_s: float = 12.0):
@@ -451,6 +475,20 @@ def main():
             extra.append(rec)
             h.close()
             del h
+            torch.cuda.empty_cache()
+        for dt in ("f16", "bf16"):
+            aw = synth.ATTN_WORKLOADS["attn_4096"]
+            at = Attn(aw, dt)
+            avg, med, mn = at.time_events(30, warm=5)
+            rec = {"workload": aw.name, "batch_heads": aw.BH, "seq_q": aw.seq_q, "seq_k": aw.seq_k,
+                   "head_dim": aw.head_dim, "dtype": dt, "us_avg": round(avg * 1e3, 2),
+                   "us_median": round(med * 1e3, 2),
+                   "tflops": round(at.flops / (avg * 1e-3) / 1e12, 2),
+                   "pct_peak": round(100 * at.flops / (avg * 1e-3) / 1e12 / PEAK_TFLOPS, 2),
+                   "bound": "mfma", "loader": "V transposed in registers (attention P*V)"}
+            log(json.dumps(rec))
+            extra.append(rec)
+            del at
             torch.cuda.empty_cache()
         out["workloads"] = extra
         out["loader_comparison"] = loader_comparison()

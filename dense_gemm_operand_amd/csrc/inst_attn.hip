@@ -18,10 +18,14 @@ int launch_attn(const AttnLaunch& l, void* stream) {
   a.q_blocks = (int)((l.Sq + 255) / 256);
   const dim3 grid((unsigned)(l.BH * a.q_blocks));
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (l.dtype == DT_F16)
-    hipLaunchKernelGGL(attn_fwd_kernel<F16T>, grid, dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL(attn_fwd_kernel<BF16T>, grid, dim3(512), 0, s, a);
+  const bool neg = l.scale < 0.f;
+  if (l.dtype == DT_F16) {
+    if (neg) hipLaunchKernelGGL((attn_fwd_kernel<F16T, true>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<F16T, false>), grid, dim3(512), 0, s, a);
+  } else {
+    if (neg) hipLaunchKernelGGL((attn_fwd_kernel<BF16T, true>), grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((attn_fwd_kernel<BF16T, false>), grid, dim3(512), 0, s, a);
+  }
   return (int)hipGetLastError();
 }
 

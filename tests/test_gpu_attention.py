@@ -120,6 +120,35 @@ def test_attention_one_hot_selects_value_rows_exactly(BH, Sq, Sk, dtype):
     assert np.array_equal(o, want)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_attention_many_tiny_weights(dtype):
+    # one key scores 0, the other 4095 score -16 ln 2: their weights 2^-16 are subnormal
+    # in fp16 and together carry 1/17 of the mass, so flushing them (in the weights' row sum
+    # or in the matrix product) would miss the bar by far
+    BH, Sq, Sk, D = 2, 64, 4096, 128
+    rng = np.random.default_rng(441)
+    q = np.zeros((BH, Sq, D))
+    q[:, :, 0] = 1.0
+    k = np.zeros((BH, Sk, D))
+    k[:, :, 0] = -16.0 * np.log(2.0)
+    k[:, 100, 0] = 0.0
+    inp = {"BH": BH, "Sq": Sq, "Sk": Sk, "D": D, "dtype": dtype, "scale": 1.0,
+           "Q": synth.to_bits(q, dtype).reshape(-1), "K": synth.to_bits(k, dtype).reshape(-1),
+           "V": synth.to_bits(rng.standard_normal((BH, Sk, D)), dtype).reshape(-1)}
+    _say("attn tiny weights", dtype)
+    check_bar(run_attn(inp), inp, what=f"tiny weights {dtype}")
+
+
+@pytest.mark.parametrize("scale", [-0.0883883476, 0.0])
+def test_attention_negative_and_zero_scale(scale):
+    # a negative scale turns the smallest score into the largest weight; a zero scale
+    # gives every key the same weight (the plain mean), also with a ragged last unit
+    _say("attn scale", scale)
+    inp = _inputs(2, 200, 333, "f16", seed=451)
+    inp["scale"] = scale
+    check_bar(run_attn(inp), inp, what=f"scale {scale}")
+
+
 def test_attention_full_size_sampled_rows():
     # the bench's workload (batch 4 x 16 heads, 4096 x 4096, head dim 128, fp16): rows of
     # the first, a middle and the last slice, at the start, middle and end of the sequence
