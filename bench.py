@@ -16,7 +16,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only-headline]
        python bench.py --copy-probe   (plain device copy of known size, for scaling
                                        rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
        python bench.py --workload NAME [--layout-a row|col --layout-b row|col] [--steps K]
-                      (only that workload, K launches: the target of per-workload profiles)
+                      (only that workload, K launches: the target of per-workload profiles;
+                       for the attention workload --layout-a gives the dtype, f16 or bf16)
 """
 from __future__ import annotations
 
@@ -332,6 +333,16 @@ def run_workload(name: str, la, lb, steps: int):
     """Only one workload, `steps` launches (rotating input sets for HBM-bound shapes)."""
     import torch
     from dense_gemm_operand_amd import synth
+    if name in synth.ATTN_WORKLOADS:
+        aw = synth.ATTN_WORKLOADS[name]
+        at = Attn(aw, la)   # --layout-a doubles as the attention dtype (f16 / bf16)
+        for _ in range(steps):
+            at.run()
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": name, "dtype": at.inp["dtype"], "launches": steps,
+                          "batch_heads": aw.BH, "seq_q": aw.seq_q, "seq_k": aw.seq_k,
+                          "head_dim": aw.head_dim}), flush=True)
+        return
     wl = synth.WORKLOADS[name]
     hbm = name in ("skinny_splitk", "int4_m16")
     g = Gemm(wl, la, lb, rotate_bytes=2 * MALL_BYTES + (64 << 20) if hbm else 0)

@@ -88,6 +88,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, kh = lane >> 5;
+  const int grp = wave >> 2;   // waves w and w + 4 share a SIMD: one of each group
 
   // Workgroup -> (slice, query block), XCD-aware: consecutive ids go round-robin over the
   // 8 XCDs, so each XCD is given a contiguous range and the query blocks of one slice
@@ -99,8 +100,12 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a) {
   const int m0 = qb * BM;
 
   const __amdgpu_buffer_rsrc_t rQ = make_rsrc(a.Q, a.bytesQ);
-  const __amdgpu_buffer_rsrc_t rK = make_rsrc(a.K, a.bytesKV);
-  const __amdgpu_buffer_rsrc_t rV = make_rsrc(a.V, a.bytesKV);
+  // K and V of this slice only: a key at or past Sk starts at or past num_records, where
+  // buffer loads return zeros, so the loads need no bounds arithmetic.
+  const size_t slice = (size_t)bh * a.Sk * D * 2;
+  const uint32_t slice_bytes = (uint32_t)a.Sk * D * 2;
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc(static_cast<const char*>(a.K) + slice, slice_bytes);
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(static_cast<const char*>(a.V) + slice, slice_bytes);
 
   // The wave's Q fragments: lane row r32 of its 32 rows, d = 16s + 8kh + 0..7.
   u32x4 q[8];
@@ -111,63 +116,52 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a) {
       q[s] = ld128(rQ, row < a.Sq ? (uint32_t)(((size_t)bh * a.Sq + row) * D + 16 * s + 8 * kh) * 2u : kOOB);
   }
 
-  // Loads of one key unit. Waves 0-3 (x = tid): V block (kh2, v, rest) = (x % 2, x / 2 % 16,
-  // x / 32): keys 4kg + j, kg = 4(rest / 2) + 2 kh2 + rest % 2, of d vector 8v. Waves 4-7
-  // (x = tid - 256): K chunk c = y % 16 of key row y / 16, y = 256 i + x (16 lanes per
-  // 256-byte row).
-  const bool v_role = wave < 4;
-  const int x = v_role ? tid : tid - 256;
-  const size_t kv0 = (size_t)bh * a.Sk;
-  const int vkh = x & 1, vv = (x >> 1) & 15, vrest = x >> 5;
+  // Each group moves half of every K and V unit: in a group, waves 0-1 (y = 0..127) take
+  // V blocks, waves 2-3 K chunks. V block z = 128 grp + y: (kh2, v, rest) = (z % 2,
+  // z / 2 % 16, z / 32): keys 4kg + j, kg = 4(rest / 2) + 2 kh2 + rest % 2, of d vector 8v.
+  // K: chunks 512 grp + 128 i + y' (i = 0..3, y' = 0..127): chunk c % 16 of key row c / 16.
+  const int gw = wave & 3;
+  const bool v_role = gw < 2;
+  const int y = (gw & 1) * 64 + lane;
+  const int vz = 128 * grp + y;
+  const int vkh = vz & 1, vv = (vz >> 1) & 15, vrest = vz >> 5;
   const int vkg = 4 * (vrest >> 1) + 2 * vkh + (vrest & 1);
+  // byte offsets within the slice at unit 0 (a unit is BN * D * 2 = 16 KiB further)
+  const uint32_t voff = (uint32_t)(4 * vkg * D + 8 * vv) * 2u;   // + 256 j
+  const int kc0 = 512 * grp + y;                                  // + 128 i
+  const uint32_t koff = (uint32_t)((kc0 >> 4) * D + 8 * (kc0 & 15)) * 2u;   // + 2048 i
   u32x4 rg[4];
-  auto load_v = [&](int unit) {
+  auto load_share = [&](int unit_k, int unit_v) {
+    if (v_role) {
+      const uint32_t u = (uint32_t)unit_v * (BN * D * 2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = unit * BN + 4 * vkg + j;
-      rg[j] = ld128(rV, key < a.Sk ? (uint32_t)((kv0 + key) * D + 8 * vv) * 2u : kOOB);
-    }
-  };
-  auto load_k = [&](int unit) {
+      for (int j = 0; j < 4; ++j) rg[j] = ld128(rV, voff + u + 256u * j);
+    } else {
+      const uint32_t u = (uint32_t)unit_k * (BN * D * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int y = 256 * i + x, key = unit * BN + (y >> 4);
-      rg[i] = ld128(rK, key < a.Sk ? (uint32_t)((kv0 + key) * D + 8 * (y & 15)) * 2u : kOOB);
+      for (int i = 0; i < 4; ++i) rg[i] = ld128(rK, koff + u + 2048u * i);
     }
   };
   // V transposed: element e of the d vector (four keys, 8 bytes) to row inv(8v + e) at
   // byte 16 rest + 8 kh2, which puts the 4-key groups of every 16 keys in order 0, 2, 1, 3.
-  auto store_v = [&](int s) {
-    char* vb = vst(s);
+  auto store_share = [&](int ks, int vs) {
+    if (v_role) {
+      char* vb = vst(vs);
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<u32x2*>(vb + PV.inv(8 * vv + e) * VPITCH + 16 * vrest + 8 * vkh) = transpose_row4(rg, e);
-  };
-  auto store_k = [&](int s) {
-    char* kb = kst(s);
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<u32x2*>(vb + PV.inv(8 * vv + e) * VPITCH + 16 * vrest + 8 * vkh) = transpose_row4(rg, e);
+    } else {
+      char* kb = kst(ks);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int y = 256 * i + x;
-      *reinterpret_cast<u32x4*>(kb + (y >> 4) * KPITCH + 16 * (y & 15)) = rg[i];
+      for (int i = 0; i < 4; ++i) {
+        const int c = kc0 + 128 * i;
+        *reinterpret_cast<u32x4*>(kb + (c >> 4) * KPITCH + 16 * (c & 15)) = rg[i];
+      }
     }
   };
 
-  // S = Q K^T for the 64 keys in K stage s: two 32-key blocks.
-  auto scores = [&](auto ST_, f32x16 (&S)[2]) {
-    const char* kb = kst(decltype(ST_)::value);
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) S[b][e] = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(kb + (32 * b + r32) * KPITCH + 16 * (2 * k + kh));
-        S[b] = mfma32x32x16<T>(kf, q[k], S[b]);
-      }
-  };
-
+  f32x16 S[2];   // scores of one unit (two 32-key blocks)
+  u32x4 pf[4];   // P fragments of that unit
   f32x16 o[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d)
@@ -179,31 +173,74 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a) {
   const float sl2 = a.scale_log2;
   constexpr float MASKED = NEG ? INFINITY : -INFINITY;
 
-  // Row maximum of S (scaled): the lane's 32 scores and its partner lane's (lane ^ 32).
-  // Masked scores (keys past Sk) are set so that they never win.
-  auto row_max = [&](f32x16 (&S)[2], int key0, auto MASK_) {
-    if constexpr (decltype(MASK_)::value) {
-      const int klim = a.Sk - key0 - 4 * kh;   // element (b, e) is valid iff its offset < klim
+  // The matrix-core phase issues the multiplies of S(k+1) and of P(k) V(k) alternately:
+  // the two score accumulators alone would make every multiply wait for the one two
+  // before it, the alternation leaves three others in between (six accumulators in turn).
+  // The fragment reads run FD multiplies ahead of their use (a ring of FD + 1
+  // fragments) and the program order is kept by scheduling fences.
+  constexpr int FD = 3;
+  // Multiply t of the phase: with scores, even t = 2s is S multiply s (k = s / 2, block
+  // b = s % 2; fragment from K stage ks) and odd t = 2s + 1 is P V multiply s (i = s / 4,
+  // d block db = s % 4; fragment from V stage vs); without, t is P V multiply t.
+  auto is_s = [](int t, bool scores) { return scores && (t & 1) == 0; };
+  auto op_idx = [](int t, bool scores) { return scores ? t >> 1 : t; };
+  auto frag_addr = [&](int t, bool scores, int ks, int vs) -> const u32x4* {
+    const int n = op_idx(t, scores);
+    if (is_s(t, scores)) {
+      const int k = n >> 1, b = n & 1;
+      return reinterpret_cast<const u32x4*>(kst(ks) + (32 * b + r32) * KPITCH + 16 * (2 * k + kh));
+    }
+    const int i = n >> 2, db = n & 3;
+    return reinterpret_cast<const u32x4*>(vst(vs) + (32 * db + r32) * VPITCH + 16 * (2 * i + kh));
+  };
+  // S(next) = Q K^T from K stage ks (if SCORES) and O += P V from V stage vs: sub-step
+  // i = 2b + u2 of P V covers keys 32b + 16u2 + 0..15; the V fragment of d block db is
+  // row 32db + r32, 16-byte chunk 2i + kh.
+  auto mma_phase = [&](int ks, int vs, auto SCORES_) {
+    constexpr bool SCORES = decltype(SCORES_)::value;
+    constexpr int NT = SCORES ? 32 : 16;
+    if constexpr (SCORES) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (32 * b + 8 * (e >> 2) + (e & 3) >= klim) S[b][e] = MASKED;
+        for (int e = 0; e < 16; ++e) S[b][e] = 0.f;
     }
-    float r = S[0][0];
+    u32x4 ring[FD + 1];
+#pragma unroll
+    for (int t = 0; t < FD; ++t) ring[t % (FD + 1)] = *frag_addr(t, SCORES, ks, vs);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + FD < NT) ring[(t + FD) % (FD + 1)] = *frag_addr(t + FD, SCORES, ks, vs);
+      const u32x4 f = ring[t % (FD + 1)];
+      const int n = op_idx(t, SCORES);
+      if (is_s(t, SCORES)) S[n & 1] = mfma32x32x16<T>(f, q[n >> 1], S[n & 1]);
+      else o[n & 3] = mfma32x32x16<T>(f, pf[n >> 2], o[n & 3]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Softmax phase of a unit starting at key0: row maximum (the lane's 32 scores and its
+  // partner lane's, keys past Sk left out), the reference update, the weights as P
+  // fragments and their row sum (the fp16/bf16 values the second product uses, added
+  // exactly in fp32 by v_dot2). The reference maximum is raised only when some row's
+  // maximum exceeds it by more than 8 (a factor 256): the weights exp2(s - m_run) then stay
+  // <= 256, well inside fp16, and the output and sums are rescaled (64 multiplies) only in
+  // those steps. The result does not depend on the reference (it cancels in O / l).
+  auto softmax = [&](int key0, auto MASK_) {
+    constexpr bool MASK = decltype(MASK_)::value;
+    const int klim = a.Sk - key0 - 4 * kh;   // element (b, e) is valid iff its offset < klim
+    auto valid = [&](int b, int e) { return 32 * b + 8 * (e >> 2) + (e & 3) < klim; };
+    float r = MASKED;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) r = NEG ? fminf(r, S[b][e]) : fmaxf(r, S[b][e]);
+      for (int e = 0; e < 16; ++e) {
+        const float v = (MASK && !valid(b, e)) ? MASKED : S[b][e];
+        r = NEG ? fminf(r, v) : fmaxf(r, v);
+      }
     r = NEG ? fminf(r, __shfl_xor(r, 32)) : fmaxf(r, __shfl_xor(r, 32));
-    return r * sl2;
-  };
-
-  // The reference maximum is raised only when some row's maximum exceeds it by more than
-  // 8 (a factor 256): the weights exp2(s - m_run) then stay <= 256, well inside fp16, and
-  // the output and sums are rescaled (64 multiplies) only in those steps. The result does
-  // not depend on which reference is used (it cancels in O / l).
-  auto rebase = [&](float mx) {
+    const float mx = r * sl2;   // finite: key0 is a valid key
     if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f) != 0) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -214,14 +251,6 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[d][e] *= alpha;
     }
-  };
-
-  // Weights of S (keys of one unit) as P fragments, their row sum (the fp16/bf16 values the
-  // second product uses, added exactly in fp32 by v_dot2), then O += P V from V stage VS.
-  auto weights_pv = [&](f32x16 (&S)[2], auto VS_, int key0, auto MASK_) {
-    constexpr bool MASK = decltype(MASK_)::value;
-    const int klim = a.Sk - key0 - 4 * kh;
-    u32x4 pf[4];   // P fragment of sub-step (b, u2): the lane's scores 8u2 .. 8u2 + 7 of block b
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -232,72 +261,71 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a) {
           float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[b][e0], sl2, -m_run));
           float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[b][e0 + 1], sl2, -m_run));
           if constexpr (MASK) {
-            p0 = 32 * b + 8 * (e0 >> 2) + (e0 & 3) < klim ? p0 : 0.f;
-            p1 = 32 * b + 8 * ((e0 + 1) >> 2) + ((e0 + 1) & 3) < klim ? p1 : 0.f;
+            p0 = valid(b, e0) ? p0 : 0.f;
+            p1 = valid(b, e0 + 1) ? p1 : 0.f;
           }
           pf[2 * b + u2][w] = pack2<T>(p0, p1);
           l_run = sum2<T>(pf[2 * b + u2][w], l_run);
         }
-    // O += P V: sub-step i = 2b + u2 covers keys 32b + 16u2 + 0..15; the V fragment of d
-    // block db is row 32db + r32, 16-byte chunk 2i + kh.
-    const char* vb = vst(decltype(VS_)::value);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const u32x4 vf = *reinterpret_cast<const u32x4*>(vb + (32 * db + r32) * VPITCH + 16 * (2 * i + kh));
-        o[db] = mfma32x32x16<T>(vf, pf[i], o[db]);
-      }
   };
 
+  // Barrier between phases, fenced so that no instruction moves from one phase into the
+  // next (matrix-core instructions have no memory effects and would drift across).
+  auto phase_end = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Ping-pong schedule. Phases: M(-1) = S(0); then per unit k: X(k) = softmax of S(k);
+  // M(k) = S(k+1) (if any) and O += P(k) V(k), this group's share of the LDS stores of
+  // K(k+2) and V(k+1) (loaded in M(k-1)) and the loads of K(k+3) and V(k+2). Every phase
+  // ends with a workgroup barrier; group 1 runs one barrier behind group 0, so on every
+  // SIMD one wave's softmax (vector ALU) overlaps the other wave's matrix-core phase.
+  // LDS lifetimes (intervals between barriers, group 0 in phase b while group 1 is in b-1):
+  // K(k+1) and V(k) are read in intervals 2k+2 and 2k+3; K(m) is stored in intervals 2m-2
+  // (group 0's half) and 2m-1 (group 1's), V(m) in 2m and 2m+1, i.e. after the last read of
+  // the unit two earlier in the same stage and before the first read.
   const int nu = (a.Sk + BN - 1) / BN;
-  const bool ragged = nu * BN != a.Sk;
-  // Prologue: K(0), V(0), K(1) into LDS, S(0) and its row maximum, then the loads of
-  // K(2) / V(1).
-  if (v_role) { load_v(0); store_v(0); } else { load_k(0); store_k(0); }
-  if (!v_role) { load_k(1); store_k(1); }
-  __syncthreads();
   using TRUE = std::integral_constant<bool, true>;
   using FALSE = std::integral_constant<bool, false>;
-  f32x16 SA[2], SB[2];
-  scores(IC<0>{}, SA);
-  float mx = (ragged && nu == 1) ? row_max(SA, 0, TRUE{}) : row_max(SA, 0, FALSE{});
-  if (v_role) load_v(1); else load_k(2);
-  __syncthreads();   // K stage 0 is rewritten in step 0
-
-  // Step j (S(j) in Sc, its row maximum in mx): S(j+1) into Sn, the weights of S(j) and
-  // O += P(j) V(j), the row maximum of S(j+1) (masked if unit j+1 is the ragged last
-  // one), the LDS stores of K(j+2) -> K stage j%2 (last read in step j-1) and V(j+1) -> V
-  // stage (j+1)%2 (last read in step j-1), the loads of the step after, one barrier.
-  // Written for even and odd j so that stages are compile-time.
-  auto step = [&](int j, auto P_, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
-    constexpr int P = decltype(P_)::value;   // j % 2
-    rebase(mx);
-    scores(IC<P ^ 1>{}, Sn);
-    weights_pv(Sc, IC<P>{}, j * BN, FALSE{});
-    mx = (ragged && j + 2 == nu) ? row_max(Sn, (j + 1) * BN, TRUE{}) : row_max(Sn, (j + 1) * BN, FALSE{});
-    if (v_role) { store_v(P ^ 1); load_v(j + 2); }
-    else { store_k(P); load_k(j + 3); }
-    __syncthreads();
-  };
-  int j = 0;
-  for (; j + 2 < nu; j += 2) {
-    step(j, IC<0>{}, SA, SB);
-    step(j + 1, IC<1>{}, SB, SA);
+  // K(0) whole (each group its half), then this group's shares of K(1) and V(0).
+  load_share(0, 0);
+  if (!v_role) store_share(0, 0);
+  load_share(1, 0);
+  __syncthreads();
+  if (grp == 1) __syncthreads();
+  // M(-1): S(0) only (the loop below handles the V part of every unit)
+  {
+    const char* kb = kst(0);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) S[b][e] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        S[b] = mfma32x32x16<T>(*reinterpret_cast<const u32x4*>(kb + (32 * b + r32) * KPITCH + 16 * (2 * k + kh)),
+                               q[k], S[b]);
   }
-  // the last unit (j = nu - 1): weights and P V only (the mask leaves a full unit whole)
-  auto last = [&](f32x16 (&Sc)[2], auto P_) {
-    rebase(mx);
-    weights_pv(Sc, P_, j * BN, TRUE{});
-  };
-  if (j + 1 < nu) {          // one more full step (j even), then the last unit (odd)
-    step(j, IC<0>{}, SA, SB);
-    ++j;
-    last(SB, IC<1>{});
-  } else {
-    last(SA, IC<0>{});
+  store_share(1, 0);
+  load_share(2, 1);
+  phase_end();
+  for (int k = 0; k + 1 < nu; ++k) {
+    softmax(k * BN, FALSE{});                       // X(k)
+    phase_end();
+    mma_phase((k + 1) & 1, k & 1, TRUE{});           // M(k)
+    store_share(k & 1, (k + 1) & 1);
+    load_share(k + 3, k + 2);
+    phase_end();
   }
-  __syncthreads();   // the output tile reuses the LDS
+  // the last unit: masked softmax, P V only (the mask leaves a full unit whole)
+  softmax((nu - 1) * BN, TRUE{});
+  phase_end();
+  mma_phase(0, (nu - 1) & 1, FALSE{});
+  phase_end();
+  if (grp == 0) __syncthreads();
 
   // ---- epilogue: row sum of both lanes, O / l, staged by logical d, 16-byte row stores
   const float l = l_run + __shfl_xor(l_run, 32);
@@ -320,7 +348,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a) {
   O_t* Og = reinterpret_cast<O_t*>(a.O);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int y = 512 * i + tid, row = y >> 4, c = y & 15;
+    const int z = 512 * i + tid, row = z >> 4, c = z & 15;
     const int gq = m0 + row;
     if (gq < a.Sq)
       *reinterpret_cast<u32x4*>(Og + ((size_t)bh * a.Sq + gq) * D + 8 * c) =
