@@ -294,12 +294,13 @@ struct Slot {
 //     eight consecutive LDS rows (eight 16-byte bank groups) times two 8-byte halves.
 //   KIND 2, block q: row q/2, K half q%2 (32 codes, 16 bytes) -> four 16-byte stores of
 //     eight binary16 weights each.
-//   KIND 3, block q: v = q % (ROWS/16), kg = q / (ROWS/16); vector j is K row 4kg + j of
-//     elements 16v..16v+15. After the byte transpose, element e's four K values (one
-//     dword) go to LDS row inv(16v + e) at byte 4kg. With the 256-row, stride-16
-//     permutation, inv(16v + e) = 16e + v: the 16 v of one store instruction land in 16
-//     rows whose 144-byte pitch puts them on 16 different 16-byte bank groups, and the
-//     four kg of the wave fill the four dwords of each group (64 different banks).
+//   KIND 3, block q = 32 h + 8 kl + vl (vl < 8, kl < 4): v = vl + 8 (h % (ROWS/128)),
+//     kg = kl + 4 (h / (ROWS/128)); vector j is K row 4kg + j of elements 16v..16v+15 (eight
+//     consecutive lanes read one 128-byte line). After the byte transpose, element e's four K
+//     values (one dword) go to LDS row inv(16v + e) at byte 4kg. With the 256-row, stride-16
+//     permutation, inv(16v + e) = 16e + v, and a row's dword offset is 36 row: the 32 lanes
+//     of one 128-byte store phase (eight v, four kg) hit dwords 36 v + kg, all different
+//     modulo 32 (and the 64 lanes of the wave all different modulo 64).
 template <int KIND, int ROWS, int THREADS, RowPerm P, int EB = 2>
 struct Operand {
   static constexpr int BK = 128 / EB;
@@ -349,7 +350,9 @@ struct Operand {
       s.kofs = 8 * kg + 4 * kh;
       s.wbase = P.inv(8 * v) * PITCH_B + 16 * kg + 8 * kh;
     } else if constexpr (KIND == 3) {
-      const int v = q % (ROWS / 16), kg = q / (ROWS / 16);
+      static_assert(ROWS % 128 == 0, "eight 16-byte vectors per store phase");
+      const int h = q >> 5;
+      const int v = (q & 7) + 8 * (h % (ROWS / 128)), kg = ((q >> 3) & 3) + 4 * (h / (ROWS / 128));
       const bool ok = live && row0 + 16 * v < rows_total;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
