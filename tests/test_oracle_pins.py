@@ -210,6 +210,36 @@ def test_dequant_every_code_against_numpy_binary16_multiply():
     assert not np.array_equal(w, two.astype(np.float64))
 
 
+@pytest.mark.parametrize("group,zero", [(32, 0), (64, 7), (256, 15), (512, 3)])
+def test_dequant_other_groups_and_zero_points(group, zero):
+    # (q - zero) * s[k // group][n] rounded once: numpy's binary16 subtract is exact here and
+    # its multiply rounds once
+    rng = np.random.default_rng(16 + group + zero)
+    K, N = 1024, 8
+    q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    s = synth.to_bits(rng.uniform(0.005, 0.02, (K // group, N)), "f16")
+    w = oracle.dequant_u4(synth.pack_u4_along_k(q), s.reshape(-1), K, N, group=group, zero=zero)
+    sv = s.view(np.float16)
+    ref = (q.astype(np.float16) - np.float16(zero)) * sv[np.arange(K) // group]
+    assert np.array_equal(w, ref.astype(np.float64))
+    # scales laid out for another group size are refused
+    if group != 128:
+        with pytest.raises(AssertionError):
+            oracle.dequant_u4(synth.pack_u4_along_k(q), s.reshape(-1), K, N, group=128, zero=zero)
+
+
+def test_dequant_group_and_zero_hand_example():
+    # K=64, N=1, group 32, zero 3: k=0 q=1 -> (1-3)*0.5; k=33 q=15 -> (15-3)*0.25
+    K, N = 64, 1
+    packed = np.full(K // 2, 0x33, dtype=np.uint8)     # q = 3 -> weight 0 elsewhere
+    packed[0] = 0x31                                    # k=0 -> q=1, k=1 -> q=3
+    packed[16] = 0xF3                                   # k=32 -> q=3, k=33 -> q=15
+    s = synth.to_bits(np.array([[0.5], [0.25]]), "f16").reshape(-1)
+    w = oracle.dequant_u4(packed, s, K, N, group=32, zero=3)[:, 0]
+    assert w[0] == (1 - 3) * 0.5 and w[33] == (15 - 3) * 0.25
+    assert np.count_nonzero(w) == 2
+
+
 def test_dequant_nibble_order_and_scale_group_hand_example():
     # K=256, N=1: byte 0 = 0x21 -> q(k=0)=1, q(k=1)=2; scales 0.5 (k<128) and 0.25 (k>=128)
     K, N = 256, 1
