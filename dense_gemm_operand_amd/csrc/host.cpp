@@ -190,7 +190,8 @@ int make_plan(Plan& p, int split_k_req) {
   if (sk > 1 && tiles > kMaxCounters) sk = 1;
   p.split_k = sk;
   // chunk: ceil(K / sk) rounded up to the per-iteration granule of the kernel
-  // int4 splits start on a scale group (the tiled code layout needs whole 128-K groups)
+  // int4 splits start on a multiple of 128 K (one skinny-kernel iteration, one block of the
+  // pre-tiled code layout); scales are looked up by absolute K, so any group size works
   const int64_t gran = p.dtype_b == DT_U4 ? 128 : v.tile_k;
   p.k_chunk = cdiv(cdiv(p.K, sk), gran) * gran;
   if (v.kernel == KERNEL_TILE) {
@@ -244,8 +245,10 @@ int gemm_plan(gemm_plan_t* out, int64_t M, int64_t N, int64_t K, int layout_a, i
   if (dtype_c == DT_U4 || dtype_c == DT_F8) return GEMM_ERR_UNSUPPORTED;
   if (dtype_b == DT_U4) {
     if (dtype_a != DT_F16 || layout_b == 0 || !quant) return GEMM_ERR_UNSUPPORTED;
-    if (quant->group_size != 128 || quant->zero_point != 8 || quant->scale_dtype != DT_F16 ||
-        quant->scale_layout != 0)
+    // group: a power of two from 32 to K dividing K; zero point 0..15
+    const int64_t g = quant->group_size;
+    if (g < 32 || (g & (g - 1)) != 0 || g > K || K % g != 0 || quant->zero_point < 0 ||
+        quant->zero_point > 15 || quant->scale_dtype != DT_F16 || quant->scale_layout != 0)
       return GEMM_ERR_UNSUPPORTED;
     if (K % 128 != 0) return GEMM_ERR_UNSUPPORTED;
   } else if (dtype_b != dtype_a) {
@@ -273,6 +276,12 @@ int gemm_plan(gemm_plan_t* out, int64_t M, int64_t N, int64_t K, int layout_a, i
   p.dtype_a = dtype_a;
   p.dtype_b = dtype_b;
   p.dtype_c = dtype_c;
+  if (dtype_b == DT_U4) {
+    int lg = 0;
+    while ((int64_t)1 << lg < quant->group_size) ++lg;
+    p.group_log2 = lg;
+    p.zero = quant->zero_point;
+  }
   const int st = make_plan(p, split_k);
   if (st != GEMM_OK) {
     delete h;

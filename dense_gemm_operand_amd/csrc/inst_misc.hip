@@ -75,7 +75,7 @@ int launch(const Plan& p, const RunArgs& r, void* stream) {
   const int64_t eb = p.dtype_a == DT_F8 ? 1 : 2;   // operand element bytes
   a.bytesA = (uint32_t)(p.M * p.K * eb);
   a.bytesB = (uint32_t)(p.dtype_b == DT_U4 ? p.N * p.K / 2 : p.N * p.K * eb);
-  a.bytesS = (uint32_t)(p.dtype_b == DT_U4 ? (p.K / 128) * p.N * 2 : 0);
+  a.bytesS = (uint32_t)(p.dtype_b == DT_U4 ? (p.K >> p.group_log2) * p.N * 2 : 0);
   a.k_chunk = (int)p.k_chunk;
   a.tiles_m = (int)((p.M + p.tile_m - 1) / p.tile_m);
   a.tiles_n = (int)((p.N + p.tile_n - 1) / p.tile_n);
@@ -83,6 +83,8 @@ int launch(const Plan& p, const RunArgs& r, void* stream) {
   const int ob = p.dtype_c == DT_F32 ? 4 : 2;
   a.c_vec = ((p.N * ob) % 16 == 0) ? 1 : 0;
   a.b_tiled = p.b_tiled;
+  a.group_log2 = p.group_log2;
+  a.zero = p.zero;
   if (p.kernel == KERNEL_SKINNY) a.c_vec = (p.N % 4 == 0) ? 1 : 0;  // 4-element stores
   return (int)all_variants()[p.variant]->fn(p, a, reinterpret_cast<hipStream_t>(stream));
 }

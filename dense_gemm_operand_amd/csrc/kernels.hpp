@@ -27,8 +27,9 @@
 // (IREE PR 19596: partial reductions left across subgroups are re-distributed through
 // shared memory into element tiles and reduced again), then across workgroups as above.
 //
-// int4 B: 4-bit codes packed two per byte along K, (q - 8) * s rounded once to binary16
-// (BitBLAS PR 268, dequantize layout example with num_elems_per_byte = 2).
+// int4 B: 4-bit codes packed two per byte along K, (q - z) * s rounded once to binary16, one
+// scale per group of K indices (BitBLAS PR 268, dequantize layout example with
+// num_elems_per_byte = 2; zero point z and group size are plan parameters).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -118,13 +119,12 @@ __device__ __forceinline__ void transpose_bytes4(uint32_t r0, uint32_t r1, uint3
 }
 
 // Eight 4-bit codes of one dword (byte b: low nibble = code of K index 2b, high nibble =
-// code of 2b+1) -> eight binary16 weights (q - 8) * s, K-consecutive, as four dwords.
-// 0x6400 | q is the binary16 encoding of 1024 + q, so subtracting 1032 gives q - 8
-// exactly; the one rounding is the binary16 multiply by s.
-__device__ __forceinline__ u32x4 dequant8(uint32_t w, f16x2 s2) {
+// code of 2b+1) -> eight binary16 weights (q - z) * s, K-consecutive, as four dwords.
+// 0x6400 | q is the binary16 encoding of 1024 + q, so subtracting bias = 1024 + z gives
+// q - z exactly; the one rounding is the binary16 multiply by s.
+__device__ __forceinline__ u32x4 dequant8(uint32_t w, f16x2 s2, f16x2 bias) {
   const uint32_t lo = w & 0x0F0F0F0Fu;
   const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
-  const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
   u32x4 r;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -142,8 +142,9 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t w, f16x2 s2) {
 // activation fragment is permuted to match): dword j holds the weights of K indices j and
 // j+4 (nibbles j and j+4). Each pair comes out of one and-or as binary16 values: a nibble
 // in bits 0..3 of a half gives 0x6400 | q = 1024 + q, one in bits 4..7 gives 1024 + 16q.
-// (1024 + q) - 1032 and (1024 + 16q) / 16 - 72 are q - 8 exactly (one fused multiply-add,
-// exact because the result is representable); the multiply by s is the single rounding.
+// (1024 + q) - (1024 + z) and (1024 + 16q) / 16 - (64 + z) are q - z exactly (one fused
+// multiply-add, exact because the result is representable); the multiply by s is the single
+// rounding. bias = -(1024 + z), bias16 = -(64 + z).
 // 13 instructions per eight weights instead of 19.
 // (x & mask) | magic in one instruction (the compiler splits it into two with literals).
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
@@ -152,16 +153,14 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t m
   return r;
 }
 
-__device__ __forceinline__ u32x4 dequant8_pairs(uint32_t w, f16x2 s2) {
+__device__ __forceinline__ u32x4 dequant8_pairs(uint32_t w, f16x2 s2, f16x2 bias, f16x2 bias16) {
   const uint32_t w8 = w >> 8;
   const uint32_t magic = 0x64006400u;
   const uint32_t t0 = and_or(w, 0x000F000Fu, magic);    // nibbles 0, 4
   const uint32_t t1 = and_or(w, 0x00F000F0u, magic);    // nibbles 1, 5 (times 16)
   const uint32_t t2 = and_or(w8, 0x000F000Fu, magic);   // nibbles 2, 6
   const uint32_t t3 = and_or(w8, 0x00F000F0u, magic);   // nibbles 3, 7 (times 16)
-  const f16x2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
   const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const f16x2 bias16 = {(_Float16)-72.0f, (_Float16)-72.0f};
   u32x4 r;
   r[0] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, t0) + bias) * s2);
   r[1] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2, t1), sixteenth, bias16) * s2);
@@ -198,7 +197,7 @@ __device__ __forceinline__ typename OutT<DT>::type cvt_out(float x) {
 struct KArgs {
   const void* A;
   const void* B;
-  const void* S;        // int4 scales (binary16, [K/128][N])
+  const void* S;        // int4 scales (binary16, [K/group][N])
   void* C;
   float* part;          // fp32 partials (split-K), after the counters
   int* counters;        // arrival counters (split-K)
@@ -210,6 +209,8 @@ struct KArgs {
   int dtype_c;
   int c_vec;            // 1 if every C row starts 16-byte aligned
   int b_tiled;          // int4 codes in the pre-tiled layout (64 columns x 128 K blocks)
+  int group_log2;       // int4: log2 of the scale group size (5 .. log2 K)
+  int zero;             // int4: zero point (0 .. 15)
 };
 
 // Split-K fix-up shared by both kernels. Every thread owns NV vectors of LEN fp32
@@ -718,7 +719,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
         rb[SET][i][j] = ld128(rB, ok ? sb[i].off[j] + d : kOOB);
         if constexpr (U4B) {
           const int gk = kb + step * BK + sb[i].kofs;
-          rs[SET][i] = ld16b(rS, (ok && sb[i].row < a.N) ? ((uint32_t)(gk / 128) * (uint32_t)a.N + sb[i].row) * 2u : kOOB);
+          rs[SET][i] = ld16b(rS, (ok && sb[i].row < a.N) ? ((uint32_t)(gk >> a.group_log2) * (uint32_t)a.N + sb[i].row) * 2u : kOOB);
         }
       }
     }
@@ -752,7 +753,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
       if constexpr (U4B) {
         const _Float16 s = __builtin_bit_cast(_Float16, rs[SET][i]);
         const f16x2 s2 = {s, s};
-        *reinterpret_cast<u32x4*>(sB + sb[i].wbase + 16 * P) = dequant8(rb[SET][i][0][P], s2);
+        const _Float16 zb = (_Float16)(1024 + a.zero);
+        const f16x2 bias = {zb, zb};
+        *reinterpret_cast<u32x4*>(sB + sb[i].wbase + 16 * P) = dequant8(rb[SET][i][0][P], s2, bias);
       } else if constexpr (B_KC) {
         *reinterpret_cast<u32x4*>(sB + sb[i].wbase + P * (MT_N / 4) * 144) = rb[SET][i][P];
       } else if constexpr (Cfg::F8) {
@@ -1231,7 +1234,9 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
       // 128 K (one iteration), 64 bytes per column
       offB0[nb] = a.b_tiled ? ((uint32_t)((n / 64) * (a.K / 128) + kb / 128) * 64u + (uint32_t)(n % 64)) * 64u + 16u * c
                             : (uint32_t)n * (uint32_t)(a.K / 2) + (uint32_t)((kb + c * KL) / 2);
-      offS0[nb] = ((uint32_t)(kb / 128) * (uint32_t)a.N + (uint32_t)n) * 2u;
+      // scale row (kb + it * KI + c * KL) / group: kb + it * KI is a multiple of 128, so the
+      // lane part c * KL and the iteration part separate (exact for every group >= 32)
+      offS0[nb] = ((uint32_t)((c * KL) >> a.group_log2) * (uint32_t)a.N + (uint32_t)n) * 2u;
     }
   }
   const uint32_t b_iter = a.b_tiled ? 4096u : (uint32_t)(KI / 2);   // B bytes per iteration
@@ -1239,7 +1244,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
     const int it = wave + j * W;
     if constexpr (U4B) {
       const uint32_t sa = (uint32_t)it * KI * 2u, sb = (uint32_t)it * b_iter;
-      const uint32_t ss = (uint32_t)it * (uint32_t)a.N * 2u;
+      const uint32_t ss = (uint32_t)((kb + it * KI) >> a.group_log2) * (uint32_t)a.N * 2u;
 #pragma unroll
       for (int h = 0; h < H; ++h)
         bufA[u][h] = __builtin_amdgcn_raw_buffer_load_b128(rA, offA0 + 16u * h, sa, 0);
@@ -1279,6 +1284,8 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
 #pragma unroll
       for (int h = 0; h < H; ++h) ap[h] = pair_k_and_k4(bufA[u][h]);
     }
+    const _Float16 zb = (_Float16)(-1024 - a.zero), zb16 = (_Float16)(-64 - a.zero);
+    const f16x2 bias = {zb, zb}, bias16 = {zb16, zb16};
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       if constexpr (U4B) {
@@ -1286,7 +1293,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
         const f16x2 s2 = {s, s};
 #pragma unroll
         for (int h = 0; h < H; ++h)
-          acc[nb] = mfma16x16x32<T>(dequant8_pairs(bufB[u][nb][0][h], s2), ap[h], acc[nb]);
+          acc[nb] = mfma16x16x32<T>(dequant8_pairs(bufB[u][nb][0][h], s2, bias, bias16), ap[h], acc[nb]);
       } else {
 #pragma unroll
         for (int h = 0; h < H; ++h)

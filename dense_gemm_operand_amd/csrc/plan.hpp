@@ -30,6 +30,8 @@ struct Plan {
   int32_t slots_per_cu = 1;
   int32_t direct_lds = 0;              // bit 0: A, bit 1: B loaded straight into LDS
   int32_t b_tiled = 0;                 // int4 codes in the pre-tiled layout (layout_b 2)
+  int32_t group_log2 = 7;              // int4: log2 of the scale group size
+  int32_t zero = 8;                    // int4: zero point
   int32_t device = -1;
 };
 

@@ -62,8 +62,9 @@ enum {
 /* Quantisation of an int4 B operand (BitBLAS PR 268, dequantize layout example:
  * num_elems_per_byte = 2). Weight w(k, n) = round_fp16((q(k, n) - zero_point) * s).
  * q(k, n) is the low nibble of byte n*(K/2) + k/2 for even k, the high nibble for odd k.
- * s = scales[(k / group_size) * N + n], binary16. Only group_size = 128, zero_point = 8,
- * scale_dtype = GEMM_F16 and scale_layout = 0 ([K/group][N] row-major) are supported. */
+ * s = scales[(k / group_size) * N + n], binary16 (K / group_size rows of N scales).
+ * Supported: group_size a power of two from 32 to K that divides K, zero_point 0..15,
+ * scale_dtype = GEMM_F16 and scale_layout = 0 ([K/group][N] row-major). */
 typedef struct {
   int32_t group_size;
   int32_t zero_point;

@@ -44,7 +44,7 @@ def to_dev(x: np.ndarray):
 
 def run_gpu(inp: dict, dtype_ab: str, dtype_c: str, split_k: int = 0, int4: bool = False,
             guard: int = 0, repeat: int = 1, force_tile: str | None = None,
-            force_split_k: int | None = None):
+            force_split_k: int | None = None, group: int = 128, zero: int = 8):
     """Plan + run C = A*B on the GPU through the C ABI; returns (C bits, plan info).
 
     ``guard`` extra sentinel elements are allocated after C and checked untouched."""
@@ -54,7 +54,7 @@ def run_gpu(inp: dict, dtype_ab: str, dtype_c: str, split_k: int = 0, int4: bool
     with env(DGEMM_FORCE_TILE=force_tile, DGEMM_FORCE_SPLIT_K=force_split_k):
         plan = dg.gemm_plan(M, N, K, inp["layout_a"], inp["layout_b"], dtype_ab,
                             "u4" if int4 else dtype_ab, dtype_c, split_k,
-                            dg.int4_quant() if int4 else None)
+                            dg.int4_quant(group, zero) if int4 else None)
     try:
         info = dg.gemm_plan_query(plan)
         A = to_dev(inp["A"])
@@ -84,11 +84,13 @@ def run_gpu(inp: dict, dtype_ab: str, dtype_c: str, split_k: int = 0, int4: bool
         dg.gemm_plan_destroy(plan)
 
 
-def reference(inp: dict, dtype_ab: str, dtype_c: str, int4: bool = False, rows=None):
+def reference(inp: dict, dtype_ab: str, dtype_c: str, int4: bool = False, rows=None,
+              group: int = 128, zero: int = 8):
     """Oracle C (fp64 sums, and bits rounded to dtype_c) for the given inputs."""
     M, N, K = inp["M"], inp["N"], inp["K"]
     return oracle.gemm(inp["A"], inp["B"], M, N, K, inp["layout_a"], inp["layout_b"], dtype_ab,
-                       dtype_c, scales_bits=inp.get("scales") if int4 else None, rows=rows)
+                       dtype_c, scales_bits=inp.get("scales") if int4 else None, rows=rows,
+                       group=group, zero=zero)
 
 
 def operand_max(inp: dict, dtype_ab: str, int4: bool = False):

@@ -86,8 +86,13 @@ def test_plan_argument_errors(fake_cus):
     assert _plan_status(64, 64, 200, ROW, COL, F16, U4, F16, 0, quant=q)[0] == dg.GEMM_ERR_UNSUPPORTED
     assert _plan_status(64, 64, 256, ROW, ROW, F16, U4, F16, 0, quant=q)[0] == dg.GEMM_ERR_UNSUPPORTED
     assert _plan_status(64, 64, 256, ROW, COL, BF16, U4, F16, 0, quant=q)[0] == dg.GEMM_ERR_UNSUPPORTED
-    q2 = dg.gemm_quant_t(64, 8, F16, 0)
-    assert _plan_status(64, 64, 256, ROW, COL, F16, U4, F16, 0, quant=q2)[0] == dg.GEMM_ERR_UNSUPPORTED
+    # group sizes: powers of two from 32 to K dividing K; zero points 0..15
+    for g, z, want in [(32, 0, dg.GEMM_OK), (64, 15, dg.GEMM_OK), (256, 3, dg.GEMM_OK),
+                       (16, 8, dg.GEMM_ERR_UNSUPPORTED), (48, 8, dg.GEMM_ERR_UNSUPPORTED),
+                       (512, 8, dg.GEMM_ERR_UNSUPPORTED), (128, 16, dg.GEMM_ERR_UNSUPPORTED),
+                       (128, -1, dg.GEMM_ERR_UNSUPPORTED)]:
+        q2 = dg.gemm_quant_t(g, z, F16, 0)
+        assert _plan_status(64, 64, 256, ROW, COL, F16, U4, F16, 0, quant=q2)[0] == want, (g, z)
     # M <= 16 with non-contiguous extents that are not multiples of 8 stay allowed where
     # the contiguous index is K
     assert _plan_status(3, 5, 64, ROW, COL, F16, F16, F16, 0)[0] == dg.GEMM_OK

@@ -250,6 +250,57 @@ def test_every_schedule_variant_bit_exact(sched, dtl, waves, la, lb):
     assert np.array_equal(c, ref)
 
 
+def _int4_group_inputs(M, N, K, group, seed):
+    # codes U{0..15} packed along K, scales [K/group][N]; A = unit rows, so C rows are
+    # dequantised weight rows exactly
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    s = synth.to_bits(rng.uniform(0.005, 0.02, (K // group, N)), "f16")
+    pick = rng.integers(0, K, size=M)
+    a = np.zeros((M, K))
+    a[np.arange(M), pick] = 1.0
+    inp = {"M": M, "N": N, "K": K, "layout_a": "row", "layout_b": "col",
+           "A": synth.store(synth.to_bits(a, "f16"), "row"), "B": synth.pack_u4_along_k(q),
+           "scales": s.reshape(-1)}
+    return inp, pick
+
+
+@pytest.mark.parametrize("group,zero", [(32, 0), (64, 15), (256, 3), (1024, 8)])
+@pytest.mark.parametrize("M,sk,tiled", [(16, 1, False), (16, 4, False), (5, 4, True),
+                                        (300, 1, False), (300, 1, True)])
+def test_int4_group_sizes_and_zero_points_bit_exact(group, zero, M, sk, tiled):
+    # skinny (M <= 16) and tiled kernels, column-major and pre-tiled codes, split-K
+    import dense_gemm_operand_amd as dg
+    N, K = 320, 2048
+    _say("int4 group/zero", group, zero, M, sk, tiled)
+    inp, pick = _int4_group_inputs(M, N, K, group, seed=700 + group + zero + M)
+    w = oracle.dequant_u4(inp["B"], inp["scales"], K, N, group=group, zero=zero)
+    if tiled:
+        inp = dict(inp, B=dg.gemm_pack_u4_tiled(inp["B"], N, K), layout_b="u4_tiled")
+    c, info = run_gpu(inp, "f16", "f16", split_k=sk, int4=True, guard=16, group=group, zero=zero)
+    assert info["kernel"] == (1 if M <= 16 else 0) and info["split_k"] == sk
+    assert np.array_equal(oracle.decode(c, "f16"), w[pick])
+
+
+@pytest.mark.parametrize("group,zero", [(32, 5), (512, 12)])
+def test_int4_group_sizes_random_within_tolerance(group, zero):
+    M, N, K = 384, 256, 1024
+    rng = np.random.default_rng(710 + group)
+    q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    s = synth.to_bits(rng.uniform(0.005, 0.02, (K // group, N)), "f16")
+    a = synth.to_bits(rng.standard_normal((M, K)), "f16")
+    inp = {"M": M, "N": N, "K": K, "layout_a": "row", "layout_b": "col",
+           "A": synth.store(a, "row"), "B": synth.pack_u4_along_k(q), "scales": s.reshape(-1)}
+    _say("int4 group random", group, zero)
+    for sk, m in ((1, M), (0, 16)):
+        sub = dict(inp, M=m, A=synth.store(a[:m], "row"))
+        c, _ = run_gpu(sub, "f16", "f16", split_k=sk, int4=True, group=group, zero=zero)
+        _, ref = reference(sub, "f16", "f16", int4=True, group=group, zero=zero)
+        amax = float(np.abs(oracle.decode(a[:m].reshape(-1), "f16")).max())
+        bmax = float(np.abs(oracle.dequant_u4(inp["B"], inp["scales"], K, N, group=group, zero=zero)).max())
+        check_tolerance(c, ref, "f16", K, amax, bmax, f"int4 g{group} z{zero} M={m}")
+
+
 INT4_SKINNY = ["4x16x2", "4x8x4", "2x8x4", "8x8x2", "2x16x4", "2x16x2", "4x8x2"]
 
 
