@@ -9,21 +9,21 @@
 // key-contiguous rows, one per d, permuted by the 64-row, stride-8 block permutation
 // (rocm-libraries PR 2487 formula) so that the stores spread over the banks.
 //
-// Workgroup: 8 waves, 256 query rows (32 per wave); keys in units of 64. Software
-// pipeline, step j (one barrier per step):
-//   1. S(j+1) = Q K(j+1)^T with v_mfma_f32_32x32x16 (Q fragments stay in registers, K
-//      fragments are 16-byte reads of [key][d] LDS rows), interleaved with
-//   2. the online softmax of S(j) (computed in step j-1) in the exp2 domain: running row
-//      maximum, partial row sums per lane, the output rescaled by exp2(m_old - m_new);
-//   3. O += P(j) V(j), with P taken straight from the score registers: a lane's score
-//      layout (keys 8g + 4*(lane/32) + c of its query row) is used as the K order of the
-//      P fragment, and V's LDS rows store each group of 16 keys in the matching order
-//      (4-key groups 0, 2, 1, 3), so a V fragment is one 16-byte read;
-//   4. LDS stores of K(j+2) and V(j+1) (loaded in step j-1: waves 0-3 load and transpose
-//      V, waves 4-7 load K, so every SIMD holds one of each), then the loads of K(j+3) and
-//      V(j+2).
-// K and V each use two LDS stages; a stage is rewritten one barrier after its last read.
-// The last step applies the key mask (keys past Sk get no weight) and computes no S(j+1).
+// Workgroup: 8 waves, 256 query rows (32 per wave); keys in units of 64. Per unit k, two
+// phases, each ending with a workgroup barrier:
+//   X(k): the online softmax of S(k) in the exp2 domain (running row maximum, partial row
+//         sums per lane, the output rescaled only when the maximum grows by more than 8),
+//         producing the P fragments: P is taken straight from the score registers (a
+//         lane's score layout, keys 8g + 4*(lane/32) + c of its query row, is used as the
+//         K order of the P fragment, and V's LDS rows store each group of 16 keys in the
+//         matching order, 4-key groups 0, 2, 1, 3, so a V fragment is one 16-byte read);
+//   M(k): S(k+1) = Q K(k+1)^T and O += P(k) V(k) with v_mfma_f32_32x32x16 (Q fragments
+//         stay in registers, K and V fragments are 16-byte LDS reads), then this wave
+//         group's half of the LDS stores of K(k+2) and V(k+1) and of the loads after them.
+// The two wave groups (waves 0-3 and 4-7; waves w and w + 4 share a SIMD) run one phase
+// apart, so on every SIMD one wave's softmax (vector ALU) runs beside the other wave's
+// matrix-core phase. K and V each use two LDS stages (lifetimes are stated with the
+// schedule below). The last unit applies the key mask (keys past Sk get no weight).
 // Epilogue: the two lanes of a row add their sums, O / l is rounded once to the output
 // type, staged through LDS in logical d order and written as 16-byte row vectors.
 #include "kernels.hpp"
@@ -173,11 +173,10 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(AttnArgs a) {
   const float sl2 = a.scale_log2;
   constexpr float MASKED = NEG ? INFINITY : -INFINITY;
 
-  // The matrix-core phase issues the multiplies of S(k+1) and of P(k) V(k) alternately:
-  // the two score accumulators alone would make every multiply wait for the one two
-  // before it, the alternation leaves three others in between (six accumulators in turn).
-  // The fragment reads run FD multiplies ahead of their use (a ring of FD + 1
-  // fragments) and the program order is kept by scheduling fences.
+  // The matrix-core phase issues the multiplies of S(k+1) and of P(k) V(k) alternately, so
+  // six accumulators take turns (no multiply depends on the one just before it). The
+  // fragment reads run FD multiplies ahead of their use (a ring of FD + 1 fragments) and the
+  // program order is kept by scheduling fences.
   constexpr int FD = 3;
   // Multiply t of the phase: with scores, even t = 2s is S multiply s (k = s / 2, block
   // b = s % 2; fragment from K stage ks) and odd t = 2s + 1 is P V multiply s (i = s / 4,
