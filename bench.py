@@ -380,7 +380,7 @@ def main():
     ap.add_argument("--layout-b", default=None)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build runs on a single MI355X and has no "
+        print(f"bench.py measures one GPU: the library runs on a single MI355X and has no "
               f"multi-GPU path (asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
     import torch
