@@ -45,9 +45,16 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_sha(path: str = KERNEL_SRC) -> str:
+    """Hash of a kernel source with comments and blank lines removed: counters taken on a
+    build stay valid across comment edits, and become stale when any code line changes."""
+    code = []
+    with open(path, encoding="utf-8") as f:
+        for ln in f:
+            ln = ln.split("//", 1)[0].rstrip()
+            if ln:
+                code.append(ln)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def read_traffic():

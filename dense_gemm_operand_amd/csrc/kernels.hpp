@@ -1,20 +1,26 @@
 #pragma once
 // HIP kernels for gfx950 (CDNA4): C = A * B with operands in any row/column-major
-// layout, fp16/bf16 (or int4 B) in, fp32 accumulate, fp32/fp16/bf16 out.
+// layout, fp16/bf16 (or int4 B, or fp8 E4M3 A and B) in, fp32 accumulate, fp32/fp16/bf16
+// out.
 //
-// Tiled kernel, per workgroup and per K step of 64:
-//   1. 128-bit buffer loads of the A and B tiles into registers. A K-contiguous operand
-//      is read as whole 128-byte row segments; an operand whose contiguous index is M or
-//      N is read with consecutive lanes on consecutive 16-byte vectors along that index,
-//      each lane taking eight consecutive K rows of its vector (the "thread rake" of
-//      Triton PR 5223, item 2), so every load instruction covers whole 128-byte lines.
-//   2. In-register transpose of such an 8x8 block of 16-bit values with byte permutes
-//      (v_perm_b32; Triton PR 5223, "Feature description"), giving eight K-contiguous
-//      16-byte vectors, one per M/N index.
-//   3. 128-bit LDS stores into padded, row-permuted, K-contiguous tiles (lds_layout.hpp).
-//   4. 128-bit LDS reads of matrix-core fragments, v_mfma_f32_32x32x16_{f16,bf16}.
-//      Two LDS stages: the global loads of step t+1 are in flight while step t's
-//      fragments are multiplied; one barrier per step.
+// Tiled kernel, per workgroup and per K step of 128 bytes per row (64 16-bit or 128 fp8 K
+// indices):
+//   1. 128-bit buffer loads. An operand whose contiguous index is M or N (transposed) is read
+//      with consecutive lanes on consecutive 16-byte vectors along that index, each lane
+//      taking four consecutive K rows of its vector (the "thread rake" of Triton PR 5223,
+//      item 2), so every load instruction covers whole 128-byte lines. A K-contiguous operand
+//      is read as whole 128-byte row segments, by default straight into LDS
+//      (buffer_load ... lds, no registers, XOR-swizzled 16-byte chunks).
+//   2. In-register transpose of each lane's 4 x 8 block of 16-bit values (4 x 16 bytes for
+//      fp8) with byte permutes (v_perm_b32; Triton PR 5223, "Feature description"), giving
+//      K-contiguous pieces per M/N index.
+//   3. LDS stores into padded, row-permuted, K-contiguous tiles (lds_layout.hpp).
+//   4. 128-bit LDS reads of matrix-core fragments, v_mfma_f32_32x32x16_{f16,bf16} or
+//      v_mfma_f32_32x32x64_f8f6f4. Two LDS stages, register loads two steps ahead,
+//      direct-to-LDS loads one step ahead, one barrier per step (or, for two transposed
+//      16-bit operands, a ping-pong of two wave groups). Optionally a transposed operand also
+//      goes straight into LDS in global order and is transposed by ds_read_b64_tr_b16
+//      (rocm-libraries PR 2487's direct-to-LDS layout with padding and row permutation).
 //   5. Split-K across workgroups (BitBLAS PR 268, "SplitK Infer"; the K origin of split
 //      z is z * k_chunk): each split stores its fp32 partial tile; the last split to
 //      arrive at the tile's counter adds all partials in ascending split order.
