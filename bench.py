@@ -305,6 +305,50 @@ def loader_comparison(rounds: int = 5, calls: int = 20) -> list:
     return res
 
 
+def vendor_blas_comparison(rounds: int = 5, calls: int = 20) -> list:
+    """Context, not a result: the 4096^3 fp16 GEMM of this library against torch.mm
+    (which dispatches to the vendor hipBLASLt kernels on ROCm) on the same operand memory
+    in each layout, timed interleaved (rounds of `calls` back-to-back launches) so that
+    the power-limited clock affects both alike."""
+    import torch
+    from dense_gemm_operand_amd import synth
+    wl = synth.WORKLOADS["square_4096"]
+    res = []
+    for la, lb in [("col", "col"), ("row", "col"), ("row", "row"), ("col", "row")]:
+        h = Gemm(wl, la, lb)
+        A, B, _ = h.sets[0]
+        M, N, K = h.M, h.N, h.K
+        # the library's layouts as torch views of the same bytes: "row" A is [M][K], "col" A
+        # is [K][M]; "col" B is [N][K], "row" B is [K][N]
+        ta = A.view(torch.float16).view(M, K) if la == "row" else A.view(torch.float16).view(K, M).t()
+        tb = B.view(torch.float16).view(N, K).t() if lb == "col" else B.view(torch.float16).view(K, N)
+        out = torch.empty(M, N, dtype=torch.float16, device="cuda")
+        runs = [h.run, lambda: torch.mm(ta, tb, out=out)]
+        t = [[], []]
+        for _ in range(rounds):
+            for i, fn in enumerate(runs):
+                for _ in range(3):
+                    fn()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(calls):
+                    fn()
+                e1.record()
+                torch.cuda.synchronize()
+                t[i].append(e0.elapsed_time(e1) * 1e3 / calls)
+        ours, blas = float(np.median(t[0])), float(np.median(t[1]))
+        rec = {"workload": wl.name, "layout_a": la, "layout_b": lb,
+               "this_library_us": round(ours, 2), "torch_mm_us": round(blas, 2),
+               "this_library_tflops": round(h.flops / (ours * 1e-6) / 1e12, 1),
+               "torch_mm_tflops": round(h.flops / (blas * 1e-6) / 1e12, 1)}
+        log(json.dumps(rec))
+        res.append(rec)
+        h.close()
+        del h, ta, tb, out
+        torch.cuda.empty_cache()
+    return res
+
+
 def int4_layout_comparison(rounds: int = 5) -> list:
     """int4 B in the column-major packing and pre-tiled (64 columns x 128 K blocks), timed
     interleaved: HIP graphs of back-to-back launches over rotating input sets for M = 16,
@@ -511,6 +555,7 @@ def main():
         out["workloads"] = extra
         out["loader_comparison"] = loader_comparison()
         out["int4_layout_comparison"] = int4_layout_comparison()
+        out["vendor_blas_comparison"] = vendor_blas_comparison()
         out["context"] = stream_context()
     print(json.dumps(out), flush=True)
 
