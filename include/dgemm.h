@@ -116,7 +116,9 @@ typedef struct {
  * dtype_c: GEMM_F32, GEMM_F16 or GEMM_BF16 (round-to-nearest-even from fp32 sums).
  * split_k: 0 lets the planner choose (waste-ratio search over the workgroup slots,
  *   i.e. CU count times resident workgroups per CU, BitBLAS PR 268 "SplitK Infer",
- *   capped at 16); otherwise 1, 2, 4, 8 or 16.
+ *   capped at 16); otherwise 1, 2, 4, 8 or 16. A factor above 1 becomes 1 when the output
+ *   has more than 16384 tiles (the capacity of the workspace's arrival counters);
+ *   gemm_plan_query reports the factor in use.
  * Constraints: M, N, K >= 1; the contiguous extent of each operand is a multiple of 16
  *   bytes, i.e. 8 16-bit or 16 fp8 elements (K for row-major A and column-major B, M for
  *   column-major A, N for row-major B); int4 needs K % 128 == 0. Violations give

@@ -132,6 +132,20 @@ def test_split_k_choice_matches_the_page_search(fake_cus, M, N, K, la, lb, dt, d
         assert info["workspace_bytes"] == 0
 
 
+def test_requested_split_k_falls_back_past_the_counter_capacity(fake_cus):
+    # one 4-byte arrival counter per output tile in the first 64 KiB of the workspace:
+    # 16384 tiles keep the requested factor, 16641 tiles (129 x 129) plan without a split
+    with env(DGEMM_FORCE_TILE="128x128"):
+        for n, want in ((16384, 4), (16512, 1)):
+            p = dg.gemm_plan(n, n, 1024, ROW, COL, F16, F16, F16, 4)
+            i = dg.gemm_plan_query(p)
+            dg.gemm_plan_destroy(p)
+            assert (i["tile_m"], i["tile_n"]) == (128, 128)
+            assert i["grid_x"] == (n // 128) ** 2
+            assert i["split_k"] == want
+            assert (i["workspace_bytes"] > 0) == (want > 1)
+
+
 def test_headline_plans(fake_cus):
     p = dg.gemm_plan(4096, 4096, 4096, COL, COL, F16, F16, F16, 0)
     i = dg.gemm_plan_query(p)
