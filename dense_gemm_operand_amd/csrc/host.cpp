@@ -259,10 +259,14 @@ int gemm_plan(gemm_plan_t* out, int64_t M, int64_t N, int64_t K, int layout_a, i
   const int64_t ca = layout_a == 0 ? K : M;
   const int64_t cb = dtype_b == DT_U4 ? K : (layout_b == 0 ? N : K);
   if ((ca * eb) % 16 != 0 || (cb * eb) % 16 != 0) return GEMM_ERR_UNSUPPORTED;
-  // 32-bit buffer offsets: every operand below 2 GiB, every size within int range
+  // 32-bit buffer offsets: every operand below 2 GiB, every size within int range. Each
+  // extent is bounded first, so that the element counts below cannot overflow; the byte
+  // limits are then compared as element counts (lim - 16 and lim divide by eb and ob).
   const int64_t lim = (int64_t)1 << 31;
   const int64_t ob = dtype_c == DT_F32 ? 4 : 2;
-  if (M * K * eb >= lim - 16 || N * K * eb >= lim - 16 || M * N * ob >= lim) return GEMM_ERR_UNSUPPORTED;
+  if (M >= lim || N >= lim || K >= lim) return GEMM_ERR_UNSUPPORTED;
+  if (M * K >= (lim - 16) / eb || N * K >= (lim - 16) / eb || M * N >= lim / ob)
+    return GEMM_ERR_UNSUPPORTED;
 
   gemm_plan_s* h = new (std::nothrow) gemm_plan_s;
   if (!h) return GEMM_ERR_INVALID_ARG;
@@ -390,8 +394,12 @@ int attn_fwd(const void* Q, const void* K, const void* V, void* O, int64_t BH, i
   if (dtype < 0 || dtype > 4 || !std::isfinite(scale)) return GEMM_ERR_INVALID_ARG;
   if (dtype != DT_F16 && dtype != DT_BF16) return GEMM_ERR_UNSUPPORTED;
   if (D != 128) return GEMM_ERR_UNSUPPORTED;
+  // every tensor below 2 GiB - 16 (32-bit buffer offsets): with each extent below 2^31 the
+  // row counts cannot overflow, and rows * D * 2 >= lim exactly when rows >= row_lim
   const int64_t lim = ((int64_t)1 << 31) - 16;
-  if (BH * Sq * D * 2 >= lim || BH * Sk * D * 2 >= lim) return GEMM_ERR_UNSUPPORTED;
+  if (BH >= lim || Sq >= lim || Sk >= lim) return GEMM_ERR_UNSUPPORTED;
+  const int64_t row_lim = (lim + 2 * D - 1) / (2 * D);
+  if (BH * Sq >= row_lim || BH * Sk >= row_lim) return GEMM_ERR_UNSUPPORTED;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return GEMM_ERR_MISALIGNED;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_ERR_NO_DEVICE;

@@ -98,6 +98,22 @@ def test_plan_argument_errors(fake_cus):
     assert _plan_status(3, 5, 64, ROW, COL, F16, F16, F16, 0)[0] == dg.GEMM_OK
 
 
+def test_plan_extents_whose_byte_counts_overflow_64_bits(fake_cus):
+    # byte counts of extents like these wrap around in 64-bit arithmetic; every one must be
+    # refused as beyond the 2 GiB operand limit, never planned
+    big = [(1 << 40, 64, 1 << 40, F16), (1 << 62, 64, 64, F16), (64, 1 << 62, 64, F16),
+           (64, 64, 1 << 62, F16), ((1 << 31) - 8, (1 << 31) - 8, 64, F32),
+           ((1 << 32) + 8, 8, 8, F16)]
+    for M, N, K, oc in big:
+        assert _plan_status(M, N, K, ROW, COL, F16, F16, oc, 0)[0] == dg.GEMM_ERR_UNSUPPORTED, (M, N, K)
+    # the limits themselves: an A of 2 GiB is refused, 256 bytes less (K - 8) is planned
+    assert _plan_status(16, 8, 1 << 26, ROW, COL, F16, F16, F16, 1)[0] == dg.GEMM_ERR_UNSUPPORTED
+    assert _plan_status(16, 8, (1 << 26) - 8, ROW, COL, F16, F16, F16, 1)[0] == dg.GEMM_OK
+    # C (fp32) at exactly 2 GiB is refused, one row less is planned
+    assert _plan_status(1 << 15, 1 << 14, 64, ROW, COL, F16, F16, F32, 1)[0] == dg.GEMM_ERR_UNSUPPORTED
+    assert _plan_status((1 << 15) - 8, 1 << 14, 64, ROW, COL, F16, F16, F32, 1)[0] == dg.GEMM_OK
+
+
 def test_plan_without_device_is_no_device():
     with env(DGEMM_FAKE_CU_COUNT=None, HIP_VISIBLE_DEVICES=None):
         import torch
@@ -336,6 +352,10 @@ def test_attention_rejects_bad_arguments_before_any_device_work():
         (ok[:8] + (F8,) + ok[9:], dg.GEMM_ERR_UNSUPPORTED),
         (ok[:4] + (64, 1 << 20) + ok[6:], dg.GEMM_ERR_UNSUPPORTED),    # Q beyond 2 GiB
         (ok[:4] + (64, 256, 1 << 20) + ok[7:], dg.GEMM_ERR_UNSUPPORTED),
+        (ok[:4] + (1 << 31, 1 << 31) + ok[6:], dg.GEMM_ERR_UNSUPPORTED),   # products wrap
+        (ok[:4] + (1, 1 << 62, 256) + ok[7:], dg.GEMM_ERR_UNSUPPORTED),
+        (ok[:4] + (1 << 62, 1, 1) + ok[7:], dg.GEMM_ERR_UNSUPPORTED),
+        (ok[:4] + (1, 1 << 23) + ok[6:], dg.GEMM_ERR_UNSUPPORTED),         # Q at 2 GiB
         ((P + 8,) + ok[1:], dg.GEMM_ERR_MISALIGNED),
         (ok[:3] + (P + 0x300002,) + ok[4:], dg.GEMM_ERR_MISALIGNED),
     ]
@@ -344,3 +364,5 @@ def test_attention_rejects_bad_arguments_before_any_device_work():
     import torch
     if not torch.cuda.is_available():
         assert L.attn_fwd(*ok) == dg.GEMM_ERR_NO_DEVICE
+        # one row below the limit passes the size checks (and stops at the device)
+        assert L.attn_fwd(*(ok[:4] + (1, (1 << 23) - 1, (1 << 23) - 1) + ok[7:])) == dg.GEMM_ERR_NO_DEVICE
