@@ -3,7 +3,9 @@
 Every function has the name of the C entry point it wraps. Device buffers are passed as
 torch tensors (or raw integer device pointers); every step of the GEMM and of the attention
 forward runs in the HIP kernels of libdgemm.so. There is no fallback: if the library is
-missing, loading fails with an error that says how to build it.
+missing, loading fails with an error that says how to build it. Tensor arguments are
+checked to be contiguous device tensors at least as large as the operation needs (the C
+ABI takes raw pointers and cannot check them); raw integer pointers are passed on as is.
 """
 from __future__ import annotations
 
@@ -106,6 +108,26 @@ def _ptr(x) -> int | None:
     return x.data_ptr()
 
 
+# Bytes that the operands of a plan made through gemm_plan occupy (A, B, scales, C), so that
+# gemm_run refuses host tensors and tensors too small for the plan before a kernel would
+# access memory outside them (the C ABI takes raw pointers and cannot check this).
+_plan_bytes: dict = {}
+
+
+def _check_buffer(x, need: int, what: str) -> None:
+    """A tensor argument must be a contiguous device tensor of at least `need` bytes; raw
+    integer pointers are passed on unchecked."""
+    if x is None or isinstance(x, int):
+        return
+    if not getattr(x, "is_cuda", False):
+        raise ValueError(f"{what}: a device tensor is needed")
+    if not x.is_contiguous():
+        raise ValueError(f"{what}: the tensor must be contiguous")
+    have = x.numel() * x.element_size()
+    if have < need:
+        raise ValueError(f"{what}: {have} bytes, {need} needed")
+
+
 def _nbytes(x) -> int:
     if x is None:
         return 0
@@ -125,6 +147,12 @@ def gemm_plan(M: int, N: int, K: int, layout_a, layout_b, dtype_a, dtype_b, dtyp
                          split_k, q)
     if st != GEMM_OK:
         raise GemmError(st, "gemm_plan")
+    da, db, dc = _code(dtype_a, DTYPE), _code(dtype_b, DTYPE), _code(dtype_c, DTYPE)
+    eb = 1 if da == GEMM_F8 else 2
+    u4 = db == GEMM_U4
+    _plan_bytes[h.value] = (M * K * eb, N * K // 2 if u4 else N * K * eb,
+                            (K // quant.group_size) * N * 2 if u4 else 0,
+                            M * N * (4 if dc == GEMM_F32 else 2))
     return h.value
 
 
@@ -149,6 +177,12 @@ def gemm_run(plan: int, A, B, scales, C, workspace=None, stream=None) -> None:
         stream = torch.cuda.current_stream().cuda_stream
     elif not isinstance(stream, int):
         stream = stream.cuda_stream
+    need = _plan_bytes.get(plan)
+    if need is not None:
+        for x, n, what in ((A, need[0], "A"), (B, need[1], "B"), (scales, need[2], "scales"),
+                           (C, need[3], "C")):
+            _check_buffer(x, n, what)
+    _check_buffer(workspace, 0, "workspace")
     st = lib().gemm_run(plan, _ptr(A), _ptr(B), _ptr(scales), _ptr(C), _ptr(workspace),
                         _nbytes(workspace), stream)
     if st != GEMM_OK:
@@ -164,6 +198,9 @@ def attn_fwd(Q, K, V, O, BH: int, Sq: int, Sk: int, D: int, dtype, scale: float,
         stream = torch.cuda.current_stream().cuda_stream
     elif not isinstance(stream, int):
         stream = stream.cuda_stream
+    if min(BH, Sq, Sk, D) > 0:
+        for x, rows, what in ((Q, Sq, "Q"), (K, Sk, "K"), (V, Sk, "V"), (O, Sq, "O")):
+            _check_buffer(x, BH * rows * D * 2, what)
     st = lib().attn_fwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), BH, Sq, Sk, D, _code(dtype, DTYPE),
                         float(scale), stream)
     if st != GEMM_OK:
@@ -179,6 +216,7 @@ def gemm_plan_query(plan: int) -> dict:
 
 
 def gemm_plan_destroy(plan: int | None) -> None:
+    _plan_bytes.pop(plan, None)
     lib().gemm_plan_destroy(plan)
 
 
@@ -195,6 +233,8 @@ def gemm_pack_u4_tiled(codes, N: int, K: int):
     pre-tiled layout; returns a new numpy uint8 array."""
     import numpy as np
     src = np.ascontiguousarray(codes, dtype=np.uint8)
+    if N > 0 and K > 0 and src.size != N * K // 2:
+        raise ValueError(f"codes: {src.size} bytes, N*K/2 = {N * K // 2} expected")
     dst = np.empty_like(src)
     st = lib().gemm_pack_u4_tiled(src.ctypes.data, dst.ctypes.data, N, K)
     if st != GEMM_OK:

@@ -366,3 +366,69 @@ def test_attention_rejects_bad_arguments_before_any_device_work():
         assert L.attn_fwd(*ok) == dg.GEMM_ERR_NO_DEVICE
         # one row below the limit passes the size checks (and stops at the device)
         assert L.attn_fwd(*(ok[:4] + (1, (1 << 23) - 1, (1 << 23) - 1) + ok[7:])) == dg.GEMM_ERR_NO_DEVICE
+
+
+class _FakeDeviceTensor:
+    """Stands in for a device tensor of `nbytes` bytes (never dereferenced: the binding
+    refuses it before calling the library)."""
+
+    is_cuda = True
+
+    def __init__(self, nbytes, contiguous=True):
+        self.nbytes, self.contig = nbytes, contiguous
+
+    def is_contiguous(self):
+        return self.contig
+
+    def numel(self):
+        return self.nbytes // 2
+
+    def element_size(self):
+        return 2
+
+    def data_ptr(self):
+        return 0x10000
+
+
+def test_binding_refuses_host_short_and_strided_tensors(fake_cus):
+    import torch
+    M = N = K = 64
+    p = dg.gemm_plan(M, N, K, ROW, COL, F16, F16, F16, 1)
+    try:
+        full = M * K * 2
+        dev = lambda n=full: _FakeDeviceTensor(n)
+        cases = [
+            ((torch.zeros(M * K, dtype=torch.int16), dev(), None, dev()), "device tensor"),
+            ((dev(), dev(), None, dev(full - 2)), "bytes"),                      # C one short
+            ((dev(full - 16), dev(), None, dev()), "bytes"),                     # A short
+            ((dev(), _FakeDeviceTensor(full, contiguous=False), None, dev()), "contiguous"),
+        ]
+        for (A, B, S, C), msg in cases:
+            with pytest.raises(ValueError, match=msg):
+                dg.gemm_run(p, A, B, S, C, stream=0)
+    finally:
+        dg.gemm_plan_destroy(p)
+    # int4 plans also size the scales: [K/group][N] fp16
+    q = dg.int4_quant(64)
+    p = dg.gemm_plan(16, 64, 256, ROW, COL, F16, "u4", F16, 1, q)
+    try:
+        with pytest.raises(ValueError, match="scales"):
+            dg.gemm_run(p, _FakeDeviceTensor(16 * 256 * 2), _FakeDeviceTensor(64 * 128),
+                        _FakeDeviceTensor((256 // 64) * 64 * 2 - 2), _FakeDeviceTensor(16 * 64 * 2),
+                        stream=0)
+    finally:
+        dg.gemm_plan_destroy(p)
+    # attention: every tensor at least BH x rows x D x 2 bytes
+    ok = lambda rows: _FakeDeviceTensor(2 * rows * 128 * 2)
+    with pytest.raises(ValueError, match="V"):
+        dg.attn_fwd(ok(300), ok(500), _FakeDeviceTensor(2 * 500 * 128 * 2 - 2), ok(300),
+                    2, 300, 500, 128, "f16", 0.125, stream=0)
+    with pytest.raises(ValueError, match="device tensor"):
+        dg.attn_fwd(ok(300), ok(500), ok(500), torch.zeros(2 * 300 * 128, dtype=torch.int16),
+                    2, 300, 500, 128, "f16", 0.125, stream=0)
+
+
+def test_pack_u4_tiled_refuses_a_short_array():
+    codes = np.zeros(64 * 128 // 2 - 1, dtype=np.uint8)
+    with pytest.raises(ValueError, match="N\\*K/2"):
+        dg.gemm_pack_u4_tiled(codes, 64, 128)
