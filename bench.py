@@ -193,8 +193,9 @@ class Attn:
 
 
 def cpu_baseline(g: Gemm, budget_s: float = 12.0):
-    """The oracle (untuned, all host threads) on a bounded sample: whole rows of the same
-    product. Also returns the rows for a parity spot check of the GPU result."""
+    """The CPU leg: the oracle (untuned, all host threads) timed on a bounded sample, whole
+    rows of the same product; the same rows then serve as a parity spot check of the GPU
+    result. Returns (baseline, spot check)."""
     import oracle
     inp, w = g.inp, g.w
     t0 = time.time()
@@ -213,15 +214,11 @@ def cpu_baseline(g: Gemm, budget_s: float = 12.0):
     c64 = oracle.gemm_f64(a, b, (r0, r0 + rows))
     dt = time.time() - t2 + prep
     flops = 2.0 * rows * g.N * g.K
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
-            "kind": "oracle",
-            "sample": f"rows {r0}..{r0 + rows - 1} of the {g.M}x{g.N}x{g.K} product "
-                      f"({flops / 1e9:.1f} GFLOP, fp64, operand decode included, {dt:.1f}s)"}, \
-        (r0, rows, c64)
-
-
-def spot_check(g: Gemm, r0: int, rows: int, c64: np.ndarray) -> dict:
-    import oracle
+    baseline = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
+                "kind": "oracle",
+                "sample": f"rows {r0}..{r0 + rows - 1} of the {g.M}x{g.N}x{g.K} product "
+                          f"({flops / 1e9:.1f} GFLOP, fp64, operand decode included, {dt:.1f}s)"}
+    # parity spot check on the sampled rows
     g.run()
     g.torch.cuda.synchronize()
     fmt = g.w.dtype_c
@@ -230,7 +227,7 @@ def spot_check(g: Gemm, r0: int, rows: int, c64: np.ndarray) -> dict:
     got = oracle.decode(raw[r0:r0 + rows], fmt)
     ref = oracle.decode(oracle.encode(c64, fmt), fmt)
     rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
-    return {"rows": rows, "rel_frobenius": rel, "ok": rel <= 1e-3}
+    return baseline, {"rows": rows, "rel_frobenius": rel, "ok": rel <= 1e-3}
 
 
 def stream_context() -> dict:
@@ -488,9 +485,7 @@ def main():
                        "kernel_avg_us": round(avg_ms * 1e3, 2),
                        "flops_per_launch": g.flops}
     if not args.no_cpu:
-        cb, (r0, rows, c64) = cpu_baseline(g)
-        out["cpu_baseline"] = cb
-        out["parity_spot_check"] = spot_check(g, r0, rows, c64)
+        out["cpu_baseline"], out["parity_spot_check"] = cpu_baseline(g)
     g.close()
     del g
     torch.cuda.empty_cache()
