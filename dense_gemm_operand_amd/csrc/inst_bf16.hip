@@ -4,10 +4,12 @@
 namespace dg {
 
 static const Variant kTable[] = {
-    // Defaults first (the planner takes the first match): direct-to-LDS loads when an
-    // operand is K-contiguous, the ping-pong schedule when both are transposed.
-    TILE_LAYOUTS_DTL(BF16T, 256, 256, 2, 4),
+    // Defaults first (the planner takes the first match): the ping-pong schedule, with
+    // direct-to-LDS loads for the K-contiguous operands (every layout but NT, which has
+    // none). The single-schedule pipeline kernels follow (DGEMM_FORCE_SCHED=0).
+    TILE_LAYOUTS_PPDTL(BF16T, 256, 256, 2, 4),
     TILE_LAYOUTS_PP(BF16T, 256, 256, 2, 4),
+    TILE_LAYOUTS_DTL(BF16T, 256, 256, 2, 4),
     TILE_LAYOUTS(BF16T, 256, 256, 2, 4),
     TILE_LAYOUTS(BF16T, 256, 256, 2, 2),
     TILE_LAYOUTS(BF16T, 192, 320, 2, 2),

@@ -627,7 +627,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   constexpr int TM = Cfg::TM, TN = Cfg::TN;
   constexpr int SA = Cfg::SA, SB = Cfg::SB;
   constexpr int SA1 = SA > 0 ? SA : 1, SB1 = SB > 0 ? SB : 1;  // array extents
-  static_assert(!(PP && Cfg::ANY_DTL), "the ping-pong schedule stores every operand itself");
+  static_assert(!(PP && (Cfg::A_TR || Cfg::B_TR)), "ping-pong: no transposing LDS reads");
   static_assert(!(PP && Cfg::F8), "the ping-pong schedule is written for 16-bit operands");
   constexpr int EB = Cfg::EB;
   constexpr RowPerm PA = Cfg::PA, PB = Cfg::PB;
@@ -1016,6 +1016,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     // load step s+2) | C(second half) | M(read first half of step s+1), with a barrier
     // after every phase. Group 1 starts one barrier late and group 0 ends with one extra
     // barrier, so both execute the same number of barriers.
+    // K-contiguous operands go straight into LDS instead (direct-to-LDS loads, no
+    // registers and no LDS stores of the threads). A wave issues its share of step t's
+    // direct loads in the memory phase that only reads (the one before the last compute
+    // phase of step t-2): two barriers after the last read of that buffer by either group.
+    // It waits for them at the end of its next storing memory phase, which comes before
+    // the barrier ahead of the first read of step t by either group.
     static_assert(WM == 2 && NS == 2, "ping-pong layout: two wave rows, one block per operand");
     const int grp = wm;
     u32x4 fa[2][TM], fb[2][TN];
@@ -1060,9 +1066,31 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
         store_part(IC<0>{}, IC<1>{}, IC<3>{});
       }
     };
+    // register loads per load_part and this wave's direct-to-LDS loads per step
+    constexpr int NREG = SA * OpA::VPB + SB * OpB::VPB;
+    constexpr int NDTL = (Cfg::A_DTL ? Cfg::DA::NI : 0) + (Cfg::B_DTL ? Cfg::DB::NI : 0);
+    // s_waitcnt vmcnt(N), no wait on the other counters. The count is by issue order: every
+    // load before the wait except the N most recent has landed. Fenced so that the loads
+    // the count assumes stay before the wait.
+    auto wait_vm = [](auto N_) {
+      constexpr int n = decltype(N_)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14));
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto dtl_fenced = [&](int step, auto BUF_) {
+      __builtin_amdgcn_sched_barrier(0);
+      dtl(step, BUF_);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (Cfg::ANY_DTL) dtl_fenced(0, IC<0>{});
     load_part(IC<0>{}, 0, IC<0>{}, IC<4>{});
     store_all(0);
     load_part(IC<0>{}, 1, IC<0>{}, IC<4>{});
+    if constexpr (Cfg::ANY_DTL) {
+      dtl_fenced(1, IC<1>{});        // buffer 1 has not been used yet
+      wait_vm(IC<NREG + NDTL>{});    // step 0 in LDS; step 1's loads may still fly
+    }
     phase_barrier();
     if (grp == 1) phase_barrier();
     readh(0, IC<0>{});
@@ -1074,23 +1102,33 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
       readh(0, IC<1>{});
       store_all(1);
       load_part(IC<0>{}, s + 2, IC<0>{}, IC<4>{});
+      if constexpr (Cfg::ANY_DTL) wait_vm(IC<NREG>{});   // step s+1's direct loads
       phase_barrier();
       compute();
       phase_barrier();
       readh(1, IC<0>{});
+      if constexpr (Cfg::ANY_DTL) dtl_fenced(s + 2, IC<0>{});
       phase_barrier();
       compute();
       phase_barrier();
       readh(1, IC<1>{});
       store_all(0);
       load_part(IC<0>{}, s + 3, IC<0>{}, IC<4>{});
+      if constexpr (Cfg::ANY_DTL) wait_vm(IC<NREG>{});   // step s+2's direct loads
       phase_barrier();
       compute();
       phase_barrier();
       readh(0, IC<0>{});
+      if constexpr (Cfg::ANY_DTL) dtl_fenced(s + 3, IC<1>{});
       phase_barrier();
     }
     if (grp == 0) phase_barrier();
+    if constexpr (Cfg::ANY_DTL) {
+      // the last direct loads (zeros past the split) still write LDS, which the epilogue
+      // reuses: every wave waits for its own, then one more barrier for all
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
 
   if (sk > 1) {
@@ -1440,6 +1478,13 @@ struct Variant {
   TILE_DTLTR(T, true, false, false, MTM, MTN, WM, WN),                                     \
   TILE_DTLTR(T, false, true, false, MTM, MTN, WM, WN),                                     \
   TILE_DTLTR(T, false, false, false, MTM, MTN, WM, WN)
+
+// Layouts with at least one K-contiguous operand: the ping-pong schedule with direct-to-LDS
+// loads for those operands.
+#define TILE_LAYOUTS_PPDTL(T, MTM, MTN, WM, WN)                                              \
+  TILE_X(T, true, true, false, MTM, MTN, WM, WN, true, true, 1),                           \
+  TILE_X(T, true, false, false, MTM, MTN, WM, WN, true, true, 1),                          \
+  TILE_X(T, false, true, false, MTM, MTN, WM, WN, true, true, 1)
 
 #define TILE_LAYOUTS_PP(T, MTM, MTN, WM, WN)                                                 \
   TILE_PP(T, true, true, false, MTM, MTN, WM, WN, true, true),                             \

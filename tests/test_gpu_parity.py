@@ -194,17 +194,18 @@ def _dtl_bits(la, lb):
     return (1 if la == "row" else 0) | (2 if lb == "col" else 0)
 
 
-@pytest.mark.parametrize("waves", [8, 4])
+@pytest.mark.parametrize("waves,sched", [(8, 1), (8, 0), (4, 0)])
 @pytest.mark.parametrize("la,lb", DTL_LAYOUTS)
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
-def test_direct_to_lds_integer_bit_exact(waves, la, lb, fmt):
-    # K-contiguous operands loaded straight into swizzled LDS rows; ragged M, N and K
-    # (K = 200: the last step has one 8-wide chunk) exercise the out-of-range zero fill
+def test_direct_to_lds_integer_bit_exact(waves, sched, la, lb, fmt):
+    # K-contiguous operands loaded straight into swizzled LDS rows, in the ping-pong (1) and
+    # the pipeline (0) schedule; ragged M, N and K (K = 200: the last step has one 8-wide
+    # chunk) exercise the out-of-range zero fill
     M, N, K = 392 + 8, 648, 200
-    _say("dtl-int", waves, la, lb, fmt)
+    _say("dtl-int", waves, sched, la, lb, fmt)
     inp = _inputs_int(M, N, K, la, lb, fmt, seed=91)
     from helpers import env
-    with env(DGEMM_FORCE_DTL=1, DGEMM_FORCE_WAVES=waves):
+    with env(DGEMM_FORCE_DTL=1, DGEMM_FORCE_WAVES=waves, DGEMM_FORCE_SCHED=sched):
         c, info = run_gpu(inp, fmt, "f32", split_k=1, force_tile="256x256", guard=64)
     assert info["direct_lds"] == _dtl_bits(la, lb) and info["waves"] == waves
     _, ref = reference(inp, fmt, "f32")
@@ -231,7 +232,7 @@ def test_direct_to_lds_split_k_and_random(la, lb):
 
 
 # Every selectable 256x256 main-loop variant: (schedule, direct-to-LDS, waves).
-SCHED_VARIANTS = [(0, 0, 8), (0, 0, 4), (1, 0, 8), (0, 1, 8), (0, 1, 4)]
+SCHED_VARIANTS = [(0, 0, 8), (0, 0, 4), (1, 0, 8), (0, 1, 8), (0, 1, 4), (1, 1, 8)]
 
 
 @pytest.mark.parametrize("sched,dtl,waves", SCHED_VARIANTS)
@@ -397,8 +398,8 @@ def test_int4_tiled_layout_bit_exact(v, M, sk):
 
 @pytest.mark.parametrize("M,N,K", [(8, 8, 16), (24, 40, 8), (264, 8, 72), (8, 520, 136)])
 @pytest.mark.parametrize("la,lb", LAYOUTS)
-@pytest.mark.parametrize("dtl", [1, 2])
-def test_direct_to_lds_mostly_out_of_range_tiles(M, N, K, la, lb, dtl):
+@pytest.mark.parametrize("dtl,sched", [(1, 1), (1, 0), (2, 0)])
+def test_direct_to_lds_mostly_out_of_range_tiles(M, N, K, la, lb, dtl, sched):
     # one 256x256 tile almost entirely past M, N or K: the out-of-range direct-to-LDS loads
     # must leave zeros (or be ignored) and the partial steps must add nothing
     from helpers import env
@@ -406,9 +407,9 @@ def test_direct_to_lds_mostly_out_of_range_tiles(M, N, K, la, lb, dtl):
         pytest.skip("no K-contiguous operand")
     if dtl == 2 and (la, lb) == ("row", "col"):
         pytest.skip("no transposed operand")
-    _say("dtl-edge", M, N, K, la, lb, dtl)
+    _say("dtl-edge", M, N, K, la, lb, dtl, sched)
     inp = _inputs_int(M, N, K, la, lb, "f16", seed=151)
-    with env(DGEMM_FORCE_DTL=dtl):
+    with env(DGEMM_FORCE_DTL=dtl, DGEMM_FORCE_SCHED=sched):
         c, info = run_gpu(inp, "f16", "f32", split_k=1, force_tile="256x256", guard=32)
     assert info["direct_lds"] != 0
     _, ref = reference(inp, "f16", "f32")
