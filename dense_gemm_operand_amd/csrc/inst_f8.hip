@@ -5,9 +5,13 @@
 namespace dg {
 
 static const Variant kTable[] = {
-    // direct-to-LDS loads for the K-contiguous operands (NN, TN, TT)
+    // Defaults first (the planner takes the first match): the ping-pong schedule, with
+    // direct-to-LDS loads for the K-contiguous operands (NN, TN, TT); NT has both operands
+    // transposed in registers.
+    TILE_LAYOUTS_PPDTL(F8T, 256, 256, 2, 4),
+    TILE_PP(F8T, false, false, false, 256, 256, 2, 4, true, true),
+    // the software-pipeline kernels (DGEMM_FORCE_SCHED=0)
     TILE_LAYOUTS_DTL(F8T, 256, 256, 2, 4),
-    // both operands transposed in registers (NT)
     TILE(F8T, false, false, false, 256, 256, 2, 4, true),
 };
 

@@ -628,7 +628,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   constexpr int SA = Cfg::SA, SB = Cfg::SB;
   constexpr int SA1 = SA > 0 ? SA : 1, SB1 = SB > 0 ? SB : 1;  // array extents
   static_assert(!(PP && (Cfg::A_TR || Cfg::B_TR)), "ping-pong: no transposing LDS reads");
-  static_assert(!(PP && Cfg::F8), "the ping-pong schedule is written for 16-bit operands");
   constexpr int EB = Cfg::EB;
   constexpr RowPerm PA = Cfg::PA, PB = Cfg::PB;
   __shared__ __attribute__((aligned(16))) u32x4 lds[Cfg::LDS_BYTES / 16];
@@ -1037,13 +1036,27 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
       }
     };
     auto compute = [&]() {
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
+      if constexpr (Cfg::F8) {
+        // one 32x32x64 multiply per block and half: its 32-byte fragment is the half's two
+        // 16-byte chunks, read as for the two 16-bit sub-steps (same chunks on A and B, so
+        // the products pair up as in the fp8 pipeline step)
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i * TN + j] = mfma32x32x16<T>(fb[q][j], fa[q][i], acc[i * TN + j]);
+          for (int j = 0; j < TN; ++j) {
+            const u32x4 a2[2] = {fa[0][i], fa[1][i]};
+            const u32x4 b2[2] = {fb[0][j], fb[1][j]};
+            acc[i * TN + j] = mfma32x32x64_f8(b2, a2, acc[i * TN + j]);
+          }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              acc[i * TN + j] = mfma32x32x16<T>(fb[q][j], fa[q][i], acc[i * TN + j]);
+      }
     };
     // Barrier between phases, fenced so the scheduler cannot move matrix-core or memory
     // instructions from one phase into another (MFMAs have no memory effects and would

@@ -34,14 +34,18 @@ def _inputs_rand(M, N, K, la, lb, seed, dist="normal1"):
     return synth.make_inputs(w, seed=seed)
 
 
+@pytest.mark.parametrize("sched", [1, 0])
 @pytest.mark.parametrize("M,N,K", [(400, 656, 208), (272, 528, 1040)])
 @pytest.mark.parametrize("la,lb", LAYOUTS)
-def test_fp8_integer_inputs_bit_exact(M, N, K, la, lb):
+def test_fp8_integer_inputs_bit_exact(M, N, K, la, lb, sched):
     # several 256x256 tiles with ragged edges in M and N; K ragged inside a 128 step, and an
-    # odd number of steps (the loop's padding step must add nothing)
-    _say("f8 int", la, lb, M, N, K)
+    # odd number of steps (the loop's padding step must add nothing); the ping-pong (1,
+    # default) and the software-pipeline (0) schedule
+    from helpers import env
+    _say("f8 int", la, lb, M, N, K, sched)
     inp = _inputs_int(M, N, K, la, lb, seed=201)
-    c, info = run_gpu(inp, "f8", "f32", split_k=1, guard=64)
+    with env(DGEMM_FORCE_SCHED=sched):
+        c, info = run_gpu(inp, "f8", "f32", split_k=1, guard=64)
     assert (info["tile_m"], info["tile_n"], info["tile_k"]) == (256, 256, 128)
     _, ref = reference(inp, "f8", "f32")
     assert np.array_equal(c, ref)
