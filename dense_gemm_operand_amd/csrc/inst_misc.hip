@@ -22,7 +22,9 @@ static const Variant kTable[] = {
     SKINNY(F16T, true, 2, 16, 4, 1),
     SKINNY(F16T, true, 2, 16, 2, 1),
     SKINNY(F16T, true, 4, 8, 2, 2),
-    // int4 B (column-major codes), A either layout
+    // int4 B (column-major codes), A either layout; row-major A: the ping-pong schedule with
+    // A loaded straight into LDS (column-major A: the pipeline, which measured faster)
+    TILE_X(F16T, true, true, true, 256, 256, 2, 4, true, true, 1),
     TILE(F16T, true, true, true, 256, 256, 2, 4, true),
     TILE(F16T, false, true, true, 256, 256, 2, 4, true),
     TILE(F16T, true, true, true, 256, 256, 2, 2, true),

@@ -1079,8 +1079,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
         store_part(IC<0>{}, IC<1>{}, IC<3>{});
       }
     };
-    // register loads per load_part and this wave's direct-to-LDS loads per step
-    constexpr int NREG = SA * OpA::VPB + SB * OpB::VPB;
+    // register loads per load_part (int4 B: a scale load per code vector too) and this
+    // wave's direct-to-LDS loads per step
+    constexpr int NREG = SA * OpA::VPB + SB * OpB::VPB * (U4B ? 2 : 1);
     constexpr int NDTL = (Cfg::A_DTL ? Cfg::DA::NI : 0) + (Cfg::B_DTL ? Cfg::DB::NI : 0);
     // s_waitcnt vmcnt(N), no wait on the other counters. The count is by issue order: every
     // load before the wait except the N most recent has landed. Fenced so that the loads

@@ -396,6 +396,32 @@ def test_int4_tiled_layout_bit_exact(v, M, sk):
     assert np.array_equal(c, ref)
 
 
+@pytest.mark.parametrize("sched", [1, 0])
+@pytest.mark.parametrize("tiled", [False, True])
+@pytest.mark.parametrize("sk", [1, 4])
+def test_int4_256_tiles_both_schedules_bit_exact(sched, tiled, sk):
+    # row-major A on 256x256 tiles: the ping-pong schedule with A loaded straight into LDS
+    # (1, the default) and the pipeline (0); ragged M and N, integer activations and
+    # power-of-two scales, so every sum is exact
+    from helpers import env
+    import dense_gemm_operand_amd as dg
+    M, N, K = 392, 384, 1152
+    _say("int4-256", sched, tiled, sk)
+    inp = _int4_inputs(M, N, K, seed=171)
+    rng = np.random.default_rng(172)
+    inp["A"] = synth.store(synth.integer_matrix(rng, M, K, -2, 2, "f16"), "row")
+    e = rng.integers(2, 7, size=(K // 128) * N)
+    inp["scales"] = synth.to_bits(np.ldexp(1.0, -e), "f16").reshape(-1)
+    _, ref = reference(inp, "f16", "f32", int4=True)
+    if tiled:
+        inp = dict(inp, B=dg.gemm_pack_u4_tiled(inp["B"], N, K), layout_b="u4_tiled")
+    with env(DGEMM_FORCE_SCHED=sched):
+        c, info = run_gpu(inp, "f16", "f32", split_k=sk, int4=True, guard=16, force_tile="256x256")
+    assert (info["tile_m"], info["split_k"]) == (256, sk)
+    assert info["direct_lds"] == (1 if sched else 0)
+    assert np.array_equal(c, ref)
+
+
 @pytest.mark.parametrize("M,N,K", [(8, 8, 16), (24, 40, 8), (264, 8, 72), (8, 520, 136)])
 @pytest.mark.parametrize("la,lb", LAYOUTS)
 @pytest.mark.parametrize("dtl,sched", [(1, 1), (1, 0), (2, 0)])
