@@ -305,8 +305,9 @@ def loader_comparison(rounds: int = 5, calls: int = 20) -> list:
 def vendor_blas_comparison(rounds: int = 5, calls: int = 20) -> list:
     """Context, not a result: the 4096^3 fp16 GEMM of this library against torch.mm
     (which dispatches to the vendor hipBLASLt kernels on ROCm) on the same operand memory
-    in each layout, timed interleaved (rounds of `calls` back-to-back launches) so that
-    the power-limited clock affects both alike."""
+    in each layout, and the fp8 E4M3 one against torch._scaled_mm in the layout it takes
+    (TN), timed interleaved (rounds of `calls` back-to-back launches) so that the
+    power-limited clock affects both alike."""
     import torch
     from dense_gemm_operand_amd import synth
     wl = synth.WORKLOADS["square_4096"]
@@ -343,6 +344,37 @@ def vendor_blas_comparison(rounds: int = 5, calls: int = 20) -> list:
         h.close()
         del h, ta, tb, out
         torch.cuda.empty_cache()
+    # fp8 E4M3: torch._scaled_mm (hipBLASLt, unit scales) takes B column-major only (TN)
+    wl8 = synth.WORKLOADS["square_4096_f8"]
+    h = Gemm(wl8, "row", "col")
+    A, B, _ = h.sets[0]
+    f8 = torch.float8_e4m3fn
+    ta = A.view(f8).view(h.M, h.K)
+    tb = B.view(f8).view(h.N, h.K).t()
+    one = torch.tensor(1.0, device="cuda")
+    runs = [h.run, lambda: torch._scaled_mm(ta, tb, scale_a=one, scale_b=one, out_dtype=torch.float16)]
+    t = [[], []]
+    for _ in range(rounds):
+        for i, fn in enumerate(runs):
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(calls):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t[i].append(e0.elapsed_time(e1) * 1e3 / calls)
+    ours, blas = float(np.median(t[0])), float(np.median(t[1]))
+    rec = {"workload": wl8.name, "layout_a": "row", "layout_b": "col",
+           "this_library_us": round(ours, 2), "torch_scaled_mm_us": round(blas, 2),
+           "this_library_tflops": round(h.flops / (ours * 1e-6) / 1e12, 1),
+           "torch_scaled_mm_tflops": round(h.flops / (blas * 1e-6) / 1e12, 1)}
+    log(json.dumps(rec))
+    res.append(rec)
+    h.close()
+    del h, ta, tb
+    torch.cuda.empty_cache()
     return res
 
 
