@@ -1017,8 +1017,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     // barrier, so both execute the same number of barriers.
     // K-contiguous operands go straight into LDS instead (direct-to-LDS loads, no
     // registers and no LDS stores of the threads). A wave issues its share of step t's
-    // direct loads in the memory phase that only reads (the one before the last compute
-    // phase of step t-2): two barriers after the last read of that buffer by either group.
+    // direct loads in the memory phase that only reads, between the last compute phase of
+    // step t-2 and the first of step t-1: two barriers after the last read of that buffer
+    // by either group.
     // It waits for them at the end of its next storing memory phase, which comes before
     // the barrier ahead of the first read of step t by either group.
     static_assert(WM == 2 && NS == 2, "ping-pong layout: two wave rows, one block per operand");
