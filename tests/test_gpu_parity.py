@@ -95,6 +95,22 @@ def test_split_k_with_empty_splits():
     assert np.array_equal(c, ref)
 
 
+@pytest.mark.parametrize("sched", [1, 0])
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_split_k_with_empty_splits_256_tiles(la, lb, sched):
+    # the 256x256 kernels (ping-pong, the default, and the pipeline): K = 256 in 16 splits of
+    # 64, so twelve splits run no K step at all (zero sums through the fix-up)
+    from helpers import env
+    M, N, K = 264, 136, 256
+    _say("empty-splits-256", la, lb, sched)
+    inp = _inputs_int(M, N, K, la, lb, "f16", seed=44)
+    with env(DGEMM_FORCE_SCHED=sched):
+        c, info = run_gpu(inp, "f16", "f32", split_k=16, force_tile="256x256", guard=16)
+    assert info["split_k"] == 16 and info["tile_m"] == 256
+    _, ref = reference(inp, "f16", "f32")
+    assert np.array_equal(c, ref)
+
+
 @pytest.mark.parametrize("M,N,K", [(16, 8192 // 8, 28672 // 8), (1, 200, 4104), (4, 1, 4096),
                                    (1, 1, 4096), (13, 24, 264)])
 @pytest.mark.parametrize("sk", [0, 1, 4])
