@@ -110,7 +110,10 @@ int make_plan(Plan& p, int split_k_req) {
   if (status != GEMM_OK) return status;
 
   const int forced = env_int("DGEMM_FORCE_VARIANT", -1);
+  // DGEMM_NO_PERM=1 takes the variant with identity LDS row order, =2 the one with identity
+  // order and unpadded 128-byte rows (comparison variants for bank-conflict measurements).
   const int no_perm = env_int("DGEMM_NO_PERM", 0);
+  const int lrows = no_perm == 2 ? 2 : (no_perm ? 0 : 1);
   int vi = -1;
   if (forced >= 0) {
     if (forced >= variant_count()) return GEMM_ERR_INVALID_ARG;
@@ -134,7 +137,7 @@ int make_plan(Plan& p, int split_k_req) {
       int64_t best = -1;
       for (const auto& t : kTiles) {
         if (force_m > 0 && (t[0] != force_m || t[1] != force_n)) continue;
-        const int v = find_variant(KERNEL_TILE, p, t[0], t[1], no_perm ? 0 : 1);
+        const int v = find_variant(KERNEL_TILE, p, t[0], t[1], lrows);
         if (v < 0) continue;
         const int64_t tiles = cdiv(p.M, t[0]) * cdiv(p.N, t[1]);
         const int64_t cost = cdiv(tiles, p.cu_count) * t[0] * t[1] * (variant_info(v).waves >= 8 ? 4 : 5);
@@ -159,12 +162,13 @@ int make_plan(Plan& p, int split_k_req) {
   // row permutation of operands transposed in registers: 64 rows, stride 8 (16-bit) or
   // 256 rows, stride 16 (fp8)
   const bool f8 = p.dtype_a == DT_F8;
-  p.perm_block = (v.kernel == KERNEL_TILE && v.perm && transposed) ? (f8 ? 256 : 64) : 1;
+  p.perm_block = (v.kernel == KERNEL_TILE && v.perm == 1 && transposed) ? (f8 ? 256 : 64) : 1;
   p.perm_stride = p.perm_block > 1 ? (f8 ? 16 : 8) : 1;
   p.lds_bytes = v.lds_bytes;
   p.slots_per_cu = v.slots_per_cu;
   p.direct_lds = v.kernel == KERNEL_TILE ? v.dtl : 0;
   if (p.direct_lds == 3) p.lds_pad = 0;  // neither operand is stored by the threads
+  if (v.kernel == KERNEL_TILE && v.perm == 2) p.lds_pad = 0;  // unpadded comparison variant
   if (p.direct_lds & 12) {
     // transposed operands in global order: 64 bytes of padding per 1 KiB LDS block and the
     // K-row permutation B = 8, S = 4

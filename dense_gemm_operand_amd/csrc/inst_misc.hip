@@ -31,11 +31,15 @@ static const Variant kTable[] = {
     TILE(F16T, false, true, true, 256, 256, 2, 2, true),
     TILE(F16T, true, true, true, 128, 128, 2, 2, true),
     TILE(F16T, false, true, true, 128, 128, 2, 2, true),
-    // identity LDS row order (for comparisons of bank conflicts)
-    TILE(F16T, false, true, false, 256, 256, 2, 4, false),
-    TILE(F16T, true, false, false, 256, 256, 2, 4, false),
-    TILE(F16T, false, true, false, 256, 256, 2, 2, false),
-    TILE(F16T, true, false, false, 256, 256, 2, 2, false),
+    // identity LDS row order (for comparisons of bank conflicts): padded rows, then
+    // unpadded 128-byte rows
+    TILE(F16T, false, true, false, 256, 256, 2, 4, 0),
+    TILE(F16T, true, false, false, 256, 256, 2, 4, 0),
+    TILE(F16T, false, true, false, 256, 256, 2, 2, 0),
+    TILE(F16T, true, false, false, 256, 256, 2, 2, 0),
+    TILE(BF16T, false, false, false, 256, 256, 2, 4, 0),
+    TILE(F16T, false, true, false, 256, 256, 2, 4, 2),
+    TILE(BF16T, false, false, false, 256, 256, 2, 4, 2),
 };
 
 int variants_misc(const Variant** out) {

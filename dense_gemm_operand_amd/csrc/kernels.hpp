@@ -308,10 +308,12 @@ struct Slot {
 //     permutation, inv(16v + e) = 16e + v, and a row's dword offset is 36 row: the 32 lanes
 //     of one 128-byte store phase (eight v, four kg) hit dwords 36 v + kg, all different
 //     modulo 32 (and the 64 lanes of the wave all different modulo 64).
-template <int KIND, int ROWS, int THREADS, RowPerm P, int EB = 2>
+template <int KIND, int ROWS, int THREADS, RowPerm P, int EB = 2, int PITCH = 144>
 struct Operand {
   static constexpr int BK = 128 / EB;
-  static constexpr int PITCH_B = 144;                // LDS row pitch: 128 B data + 16 B pad
+  // LDS row pitch: 128 B of data plus 16 B of padding (128: no padding, a comparison
+  // variant whose fragment reads and transposed stores meet bank conflicts)
+  static constexpr int PITCH_B = PITCH;
   static constexpr int VPB = KIND == 2 ? 1 : 4;
   static constexpr int BLOCKS = ROWS * 2;            // blocks per K step
   static constexpr int SLOTS = (BLOCKS + THREADS - 1) / THREADS;
@@ -331,6 +333,8 @@ struct Operand {
   static_assert((KIND != 1 && KIND != 2) || EB == 2, "16-bit operand kinds");
   static_assert(KIND != 3 || EB == 1, "fp8 operand kind");
   static_assert(!(PARTIAL && KIND == 2), "int4 blocks must fill every thread");
+  static_assert(PITCH == 144 || (PITCH == 128 && !PARTIAL && KIND != 2),
+                "unpadded rows: no idle lanes (they store into the padding), no int4");
 
   // Block q of this K split: offsets, K offset and LDS base. Blocks past BLOCKS (idle
   // lanes of a partial slot) read nothing (zeros) and store them into padding bytes of
@@ -518,8 +522,11 @@ __device__ __forceinline__ u32x4 tr_fragment(const char* p) {
   return u32x4{a[0], a[1], b[0], b[1]};
 }
 
+// LROWS, the LDS rows of operands stored by the threads: 1 = permuted (transposed operands)
+// and padded, 0 = identity order and padded, 2 = identity order without padding. 0 and 2
+// are comparison variants for bank-conflict measurements.
 template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN,
-          bool PERM, int DTL>
+          int LROWS, int DTL>
 struct TileCfg {
   static constexpr int EB = elem_bytes<T>();
   static constexpr bool F8 = EB == 1;
@@ -538,11 +545,14 @@ struct TileCfg {
   static constexpr bool ANY_DTL = A_DTL || B_DTL || A_TR || B_TR;
   // LDS row permutation of an operand transposed in registers (see Operand).
   static constexpr RowPerm PT = F8 ? RowPerm{256, 16} : RowPerm{64, 8};
-  static constexpr RowPerm PA = (!A_KC && PERM && !A_TR) ? PT : RowPerm{1, 1};
-  static constexpr RowPerm PB = (!B_KC && !U4B && PERM && !B_TR) ? PT : RowPerm{1, 1};
+  static constexpr RowPerm PA = (!A_KC && LROWS == 1 && !A_TR) ? PT : RowPerm{1, 1};
+  static constexpr RowPerm PB = (!B_KC && !U4B && LROWS == 1 && !B_TR) ? PT : RowPerm{1, 1};
+  static_assert(LROWS >= 0 && LROWS <= 2 && (LROWS != 2 || (DTL == 0 && !U4B)),
+                "unpadded rows: a comparison variant of the register-staged kernels");
+  static constexpr int PITCH = LROWS == 2 ? 128 : 144;
   static constexpr int KT = F8 ? 3 : 1;                  // kind of a transposed operand
-  using OpA = Operand<A_KC ? 0 : KT, MT_M, THREADS, PA, EB>;
-  using OpB = Operand<U4B ? 2 : (B_KC ? 0 : KT), MT_N, THREADS, PB, EB>;
+  using OpA = Operand<A_KC ? 0 : KT, MT_M, THREADS, PA, EB, PITCH>;
+  using OpB = Operand<U4B ? 2 : (B_KC ? 0 : KT), MT_N, THREADS, PB, EB, PITCH>;
   using DA = DtlOperand<MT_M, THREADS, EB>;
   using DB = DtlOperand<MT_N, THREADS, EB>;
   using TA = DtlTrOperand<A_TR ? MT_M : 256, THREADS>;
@@ -552,7 +562,7 @@ struct TileCfg {
   static constexpr int SB = (B_DTL || B_TR) ? 0 : OpB::SLOTS;
   // LDS row pitch in 16-byte units: 128 B of data, plus 16 B of padding for operands
   // stored by the threads (none for direct-to-LDS rows, which use the chunk swizzle).
-  static constexpr int PA16 = A_DTL ? 8 : 9, PB16 = B_DTL ? 8 : 9;
+  static constexpr int PA16 = A_DTL ? 8 : PITCH / 16, PB16 = B_DTL ? 8 : PITCH / 16;
   static constexpr int A16 = A_TR ? TA::BYTES / 16 : MT_M * PA16;
   static constexpr int B16 = B_TR ? TB::BYTES / 16 : MT_N * PB16;
   static constexpr int STAGE16 = A16 + B16;
@@ -617,9 +627,9 @@ constexpr bool epilogue_runs16_ok() {
 }
 
 template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN,
-          bool PERM, bool PP, int DTL>
+          int LROWS, bool PP, int DTL>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
-  using Cfg = TileCfg<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, PERM, DTL>;
+  using Cfg = TileCfg<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, LROWS, DTL>;
   using OpA = typename Cfg::OpA;
   using OpB = typename Cfg::OpB;
   constexpr int BK = Cfg::BK, THREADS = Cfg::THREADS;
@@ -739,18 +749,18 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
 #pragma unroll
     for (int i = 0; i < SA; ++i) {
       if constexpr (A_KC) {
-        *reinterpret_cast<u32x4*>(sA + sa[i].wbase + P * (MT_M / 4) * 144) = ra[SET][i][P];
+        *reinterpret_cast<u32x4*>(sA + sa[i].wbase + P * (MT_M / 4) * OpA::PITCH_B) = ra[SET][i][P];
       } else if constexpr (Cfg::F8) {
         // elements 4P..4P+3 of the block's 16-byte vectors
         uint32_t o[4];
         transpose_bytes4(ra[SET][i][0][P], ra[SET][i][1][P], ra[SET][i][2][P], ra[SET][i][3][P], o);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          *reinterpret_cast<uint32_t*>(sA + sa[i].wbase + (4 * P + e) * OpA::ES * 144) = o[e];
+          *reinterpret_cast<uint32_t*>(sA + sa[i].wbase + (4 * P + e) * OpA::ES * OpA::PITCH_B) = o[e];
       } else {
 #pragma unroll
         for (int e = 2 * P; e < 2 * P + 2; ++e)
-          *reinterpret_cast<u32x2*>(sA + sa[i].wbase + e * OpA::ES * 144) = transpose_row4(ra[SET][i], e);
+          *reinterpret_cast<u32x2*>(sA + sa[i].wbase + e * OpA::ES * OpA::PITCH_B) = transpose_row4(ra[SET][i], e);
       }
     }
 #pragma unroll
@@ -762,17 +772,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
         const f16x2 bias = {zb, zb};
         *reinterpret_cast<u32x4*>(sB + sb[i].wbase + 16 * P) = dequant8(rb[SET][i][0][P], s2, bias);
       } else if constexpr (B_KC) {
-        *reinterpret_cast<u32x4*>(sB + sb[i].wbase + P * (MT_N / 4) * 144) = rb[SET][i][P];
+        *reinterpret_cast<u32x4*>(sB + sb[i].wbase + P * (MT_N / 4) * OpB::PITCH_B) = rb[SET][i][P];
       } else if constexpr (Cfg::F8) {
         uint32_t o[4];
         transpose_bytes4(rb[SET][i][0][P], rb[SET][i][1][P], rb[SET][i][2][P], rb[SET][i][3][P], o);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          *reinterpret_cast<uint32_t*>(sB + sb[i].wbase + (4 * P + e) * OpB::ES * 144) = o[e];
+          *reinterpret_cast<uint32_t*>(sB + sb[i].wbase + (4 * P + e) * OpB::ES * OpB::PITCH_B) = o[e];
       } else {
 #pragma unroll
         for (int e = 2 * P; e < 2 * P + 2; ++e)
-          *reinterpret_cast<u32x2*>(sB + sb[i].wbase + e * OpB::ES * 144) = transpose_row4(rb[SET][i], e);
+          *reinterpret_cast<u32x2*>(sB + sb[i].wbase + e * OpB::ES * OpB::PITCH_B) = transpose_row4(rb[SET][i], e);
       }
     }
   };
@@ -1433,12 +1443,12 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
 
 using LaunchFn = hipError_t (*)(const Plan&, const KArgs&, hipStream_t);
 
-template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN, bool PERM,
+template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN, int LROWS,
           bool PP, int DTL>
 hipError_t launch_tile(const Plan& p, const KArgs& a, hipStream_t s) {
-  using Cfg = TileCfg<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, PERM, DTL>;
+  using Cfg = TileCfg<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, LROWS, DTL>;
   dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.grid_z);
-  hipLaunchKernelGGL((gemm_tile_kernel<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, PERM, PP, DTL>),
+  hipLaunchKernelGGL((gemm_tile_kernel<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, LROWS, PP, DTL>),
                      grid, dim3(Cfg::THREADS), 0, s, a);
   return hipGetLastError();
 }

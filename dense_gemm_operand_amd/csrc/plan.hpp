@@ -56,7 +56,9 @@ struct VariantInfo {
   int32_t tile_m, tile_n, tile_k;
   int32_t waves;
   int32_t wave_split_k;
-  int32_t perm;                   // 1 = permuted LDS rows for transposed operands
+  int32_t perm;                   // LDS rows of thread-stored operands: 1 = permuted (transposed
+                                  // operands) and padded, 0 = identity order, padded, 2 = identity
+                                  // order, unpadded
   int32_t lds_bytes;
   int32_t depth;                  // skinny: K iterations in flight per wave
   int32_t slots_per_cu;           // workgroups assumed resident per CU by the split-K search

@@ -180,17 +180,23 @@ def test_int4_random_within_tolerance(M, la):
     check_tolerance(c, ref, "f16", K, amax, bmax, "int4")
 
 
-def test_no_permutation_variant_matches():
-    # the identity-row-order variant gives the same bits as the permuted one
-    M, N, K = 512, 512, 256
-    _say("perm-off")
-    inp = _inputs_int(M, N, K, "col", "col", "f16", seed=71)
+@pytest.mark.parametrize("dt,la,lb", [("f16", "col", "col"), ("bf16", "col", "row")])
+@pytest.mark.parametrize("no_perm", [1, 2])
+def test_no_permutation_variant_matches(dt, la, lb, no_perm):
+    # the identity-row-order variants (padded rows, and unpadded 128-byte rows) give the
+    # same bits as the permuted default on integer inputs; ragged M and N edges included
+    M, N, K = 520, 488, 320
+    _say("perm-off", dt, la, lb, no_perm)
+    inp = _inputs_int(M, N, K, la, lb, dt, seed=71)
     from helpers import env
-    with env(DGEMM_NO_PERM=1):
-        c0, i0 = run_gpu(inp, "f16", "f32", split_k=1, force_tile="256x256")
-    c1, i1 = run_gpu(inp, "f16", "f32", split_k=1, force_tile="256x256")
+    with env(DGEMM_NO_PERM=no_perm):
+        c0, i0 = run_gpu(inp, dt, "f32", split_k=1, force_tile="256x256")
+    c1, i1 = run_gpu(inp, dt, "f32", split_k=1, force_tile="256x256")
     assert i0["perm_block"] == 1 and i1["perm_block"] == 64
+    assert i0["lds_pad_bytes"] == (0 if no_perm == 2 else 16)
     assert np.array_equal(c0, c1)
+    _, ref = reference(inp, dt, "f32")
+    assert np.array_equal(c0, ref)
 
 
 @pytest.mark.parametrize("M,N,K", [(8, 8, 8), (8, 16, 64), (24, 40, 16)])
