@@ -261,20 +261,24 @@ def stream_context() -> dict:
 def loader_comparison(rounds: int = 5, calls: int = 20) -> list:
     """The two loaders for transposed operands on the same shapes, timed interleaved
     (rounds of `calls` back-to-back launches, alternating) so that clock drift on the box
-    affects both alike: the in-register transpose (default) and direct-to-LDS loads in
-    global order transposed by the LDS reads (planner hook DGEMM_FORCE_DTL=2)."""
+    affects both alike: the in-register transpose (the default where one operand is
+    K-contiguous; planner hook DGEMM_FORCE_DTL=0 where none is) and direct-to-LDS loads in
+    global order transposed by the LDS reads (DGEMM_FORCE_DTL=2; the default for NT)."""
     import torch
     from dense_gemm_operand_amd import synth
     res = []
     for name, la, lb in [("square_4096", "col", "col"), ("square_4096", "row", "row"),
                          ("square_4096", "col", "row"), ("nonpow2_bf16", None, None)]:
         wl = synth.WORKLOADS[name]
-        hs = [Gemm(wl, la, lb)]
-        os.environ["DGEMM_FORCE_DTL"] = "2"
-        try:
-            hs.append(Gemm(wl, la, lb))
-        finally:
-            os.environ.pop("DGEMM_FORCE_DTL", None)
+        hs = []
+        nt = (la or wl.layout_a) == "col" and (lb or wl.layout_b) == "row"
+        for dtl in ("0" if nt else None, "2"):
+            if dtl is not None:
+                os.environ["DGEMM_FORCE_DTL"] = dtl
+            try:
+                hs.append(Gemm(wl, la, lb))
+            finally:
+                os.environ.pop("DGEMM_FORCE_DTL", None)
         t = [[], []]
         for _ in range(rounds):
             for i, h in enumerate(hs):

@@ -372,6 +372,7 @@ int gemm_plan_query(gemm_plan_t plan, gemm_plan_info_t* info) {
   info->cu_count = p.cu_count;
   info->slots_per_cu = p.slots_per_cu;
   info->direct_lds = p.direct_lds;
+  info->schedule = p.kernel == dg::KERNEL_TILE ? dg::variant_info(p.variant).sched : 0;
   return GEMM_OK;
 }
 

@@ -5,9 +5,13 @@ namespace dg {
 
 static const Variant kTable[] = {
     // Defaults first (the planner takes the first match): the ping-pong schedule, with
-    // direct-to-LDS loads for the K-contiguous operands (every layout but NT, which has
-    // none). The single-schedule pipeline kernels follow (DGEMM_FORCE_SCHED=0).
+    // direct-to-LDS loads for the K-contiguous operands (TN, TT, NN: the transposed operand
+    // goes through the in-register transpose); for NT, where both operands are transposed,
+    // both go straight into LDS and are transposed by the LDS reads (the in-register
+    // transpose of both measured 11-18% slower; DGEMM_FORCE_DTL=0 selects it). The
+    // single-schedule pipeline kernels follow (DGEMM_FORCE_SCHED=0).
     TILE_LAYOUTS_PPDTL(BF16T, 256, 256, 2, 4),
+    TILE_X(BF16T, false, false, false, 256, 256, 2, 4, true, true, 2),
     TILE_LAYOUTS_PP(BF16T, 256, 256, 2, 4),
     TILE_LAYOUTS_DTL(BF16T, 256, 256, 2, 4),
     TILE_LAYOUTS(BF16T, 256, 256, 2, 4),

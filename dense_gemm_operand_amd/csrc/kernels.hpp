@@ -637,7 +637,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   constexpr int TM = Cfg::TM, TN = Cfg::TN;
   constexpr int SA = Cfg::SA, SB = Cfg::SB;
   constexpr int SA1 = SA > 0 ? SA : 1, SB1 = SB > 0 ? SB : 1;  // array extents
-  static_assert(!(PP && (Cfg::A_TR || Cfg::B_TR)), "ping-pong: no transposing LDS reads");
   constexpr int EB = Cfg::EB;
   constexpr RowPerm PA = Cfg::PA, PB = Cfg::PB;
   __shared__ __attribute__((aligned(16))) u32x4 lds[Cfg::LDS_BYTES / 16];
@@ -1026,7 +1025,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     // after every phase. Group 1 starts one barrier late and group 0 ends with one extra
     // barrier, so both execute the same number of barriers.
     // K-contiguous operands go straight into LDS instead (direct-to-LDS loads, no
-    // registers and no LDS stores of the threads). A wave issues its share of step t's
+    // registers and no LDS stores of the threads), and so do transposed operands in the
+    // variant that transposes them with the LDS reads. A wave issues its share of step t's
     // direct loads in the memory phase that only reads, between the last compute phase of
     // step t-2 and the first of step t-1: two barriers after the last read of that buffer
     // by either group.
@@ -1038,12 +1038,23 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     auto readh = [&](int buf, auto H_) {
       constexpr int H = decltype(H_)::value;
       const u32x4* st = lds + buf * Cfg::STAGE16;
+      const char* sbytes = reinterpret_cast<const char*>(st);
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa[q][i] = st[a_rd[2 * H + q] + i * 32 * PA16];
+        for (int i = 0; i < TM; ++i) {
+          if constexpr (Cfg::A_TR)
+            fa[q][i] = tr_fragment(sbytes + a_tr + 8 * Cfg::TA::BLOCK_BYTES * (2 * H + q) + 64 * i);
+          else
+            fa[q][i] = st[a_rd[2 * H + q] + i * 32 * PA16];
+        }
 #pragma unroll
-        for (int j = 0; j < TN; ++j) fb[q][j] = st[b_rd[2 * H + q] + j * 32 * PB16];
+        for (int j = 0; j < TN; ++j) {
+          if constexpr (Cfg::B_TR)
+            fb[q][j] = tr_fragment(sbytes + b_tr + 8 * Cfg::TB::BLOCK_BYTES * (2 * H + q) + 64 * j);
+          else
+            fb[q][j] = st[b_rd[2 * H + q] + j * 32 * PB16];
+        }
       }
     };
     auto compute = [&]() {
@@ -1093,7 +1104,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     // register loads per load_part (int4 B: a scale load per code vector too) and this
     // wave's direct-to-LDS loads per step
     constexpr int NREG = SA * OpA::VPB + SB * OpB::VPB * (U4B ? 2 : 1);
-    constexpr int NDTL = (Cfg::A_DTL ? Cfg::DA::NI : 0) + (Cfg::B_DTL ? Cfg::DB::NI : 0);
+    constexpr int NDTL = (Cfg::A_DTL ? Cfg::DA::NI : 0) + (Cfg::B_DTL ? Cfg::DB::NI : 0) +
+                         (Cfg::A_TR ? Cfg::TA::NI : 0) + (Cfg::B_TR ? Cfg::TB::NI : 0);
+    static_assert(NREG + NDTL < 64, "vmcnt field");
     // s_waitcnt vmcnt(N), no wait on the other counters. The count is by issue order: every
     // load before the wait except the N most recent has landed. Fenced so that the loads
     // the count assumes stay before the wait.
@@ -1510,6 +1523,13 @@ struct Variant {
   TILE_X(T, true, true, false, MTM, MTN, WM, WN, true, true, 1),                           \
   TILE_X(T, true, false, false, MTM, MTN, WM, WN, true, true, 1),                          \
   TILE_X(T, false, true, false, MTM, MTN, WM, WN, true, true, 1)
+
+// Layouts with at least one transposed operand: the ping-pong schedule with every operand
+// loaded straight into LDS, the transposed ones in global order, transposed by the LDS reads.
+#define TILE_LAYOUTS_PPTR(T, MTM, MTN, WM, WN)                                               \
+  TILE_X(T, true, false, false, MTM, MTN, WM, WN, true, true, 2),                          \
+  TILE_X(T, false, true, false, MTM, MTN, WM, WN, true, true, 2),                          \
+  TILE_X(T, false, false, false, MTM, MTN, WM, WN, true, true, 2)
 
 #define TILE_LAYOUTS_PP(T, MTM, MTN, WM, WN)                                                 \
   TILE_PP(T, true, true, false, MTM, MTN, WM, WN, true, true),                             \

@@ -101,6 +101,9 @@ typedef struct {
                               straight into LDS in global order (1 KiB blocks of two K rows
                               plus lds_pad_bytes = 64, K rows permuted with perm_block = 8,
                               perm_stride = 4) and transposed by the LDS reads */
+  int32_t schedule;        /* tiled kernel's main loop: 0 = one software pipeline for all
+                              waves, 1 = two wave groups in ping-pong (one multiplies while
+                              the other reads LDS); 0 for the skinny kernel */
 } gemm_plan_info_t;
 
 /* Make a plan for C (M x N, row-major, dtype_c) = A (M x K) * B (K x N).

@@ -137,6 +137,7 @@ def test_split_k_choice_matches_the_page_search(fake_cus, M, N, K, la, lb, dt, d
     info = dg.gemm_plan_query(p)
     dg.gemm_plan_destroy(p)
     step = info["tile_k"] * (info["waves"] if info["kernel"] == 1 else 1)
+    assert info["kernel"] == 0 or info["schedule"] == 0   # the skinny kernel has one loop
     want = oracle.splitk_factor(M, N, K, info["tile_m"], info["tile_n"], step,
                                 256 * info["slots_per_cu"])
     assert info["split_k"] == want
@@ -169,6 +170,7 @@ def test_headline_plans(fake_cus):
     assert (i["tile_m"], i["tile_n"], i["split_k"], i["grid_x"]) == (256, 256, 1, 256)
     assert (i["perm_block"], i["perm_stride"], i["lds_pad_bytes"]) == (64, 8, 16)
     assert i["direct_lds"] == 2   # B (column-major, K-contiguous) goes straight to LDS
+    assert i["schedule"] == 1     # two wave groups in ping-pong
     assert i["lds_bytes"] <= 160 * 1024
     # 3072x5120: the 8-wave 256x256 kernel (240 tiles) is charged less than the 4-wave
     # 192x320 one (256 tiles); at 2880x5440 (264 tiles of 256x256, two rounds on 256 CUs,

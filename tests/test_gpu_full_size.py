@@ -86,16 +86,21 @@ def _perm_inputs(which: str, la: str, lb: str, seed: int):
 
 @pytest.mark.parametrize("which", ["A", "B"])
 @pytest.mark.parametrize("la,lb", [("col", "col"), ("col", "row"), ("row", "col"), ("row", "row")])
-@pytest.mark.parametrize("loader", ["default", "transposing_reads"])
+@pytest.mark.parametrize("loader", ["default", "transposing_reads", "in_register"])
 def test_full_size_permutation_every_element(which, la, lb, loader):
     # 4096^3 as the bench runs it: every element of C must be the exact permuted entry
     if loader == "transposing_reads" and la == "row" and lb == "col":
         pytest.skip("no transposed operand")
+    if loader == "in_register" and (la, lb) != ("col", "row"):
+        pytest.skip("the default already transposes in registers")
     _say("full perm", which, la, lb, loader)
     inp, want = _perm_inputs(which, la, lb, seed=111 + (which == "B"))
-    with env(DGEMM_FORCE_DTL=2 if loader == "transposing_reads" else None):
+    force = {"default": None, "transposing_reads": 2, "in_register": 0}[loader]
+    with env(DGEMM_FORCE_DTL=force):
         c, info = run_gpu(inp, "f16", "f16", split_k=1, guard=16)
-    assert ((info["direct_lds"] & 12) != 0) == (loader == "transposing_reads")
+    # NT (both operands transposed) takes the transposing reads by default
+    want_tr = loader == "transposing_reads" or (loader == "default" and (la, lb) == ("col", "row"))
+    assert ((info["direct_lds"] & 12) != 0) == want_tr
     assert np.array_equal(c, want)
 
 

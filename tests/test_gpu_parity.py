@@ -191,7 +191,9 @@ def test_no_permutation_variant_matches(dt, la, lb, no_perm):
     from helpers import env
     with env(DGEMM_NO_PERM=no_perm):
         c0, i0 = run_gpu(inp, dt, "f32", split_k=1, force_tile="256x256")
-    c1, i1 = run_gpu(inp, dt, "f32", split_k=1, force_tile="256x256")
+    # the permuted in-register kernel (NT's default transposes with the LDS reads instead)
+    with env(DGEMM_FORCE_DTL=0 if (la, lb) == ("col", "row") else None):
+        c1, i1 = run_gpu(inp, dt, "f32", split_k=1, force_tile="256x256")
     assert i0["perm_block"] == 1 and i1["perm_block"] == 64
     assert i0["lds_pad_bytes"] == (0 if no_perm == 2 else 16)
     assert np.array_equal(c0, c1)
@@ -254,21 +256,25 @@ def test_direct_to_lds_split_k_and_random(la, lb):
 
 
 # Every selectable 256x256 main-loop variant: (schedule, direct-to-LDS, waves).
-SCHED_VARIANTS = [(0, 0, 8), (0, 0, 4), (1, 0, 8), (0, 1, 8), (0, 1, 4), (1, 1, 8)]
+SCHED_VARIANTS = [(0, 0, 8), (0, 0, 4), (1, 0, 8), (0, 1, 8), (0, 1, 4), (1, 1, 8), (0, 2, 8),
+                  (1, 2, 8)]
 
 
 @pytest.mark.parametrize("sched,dtl,waves", SCHED_VARIANTS)
 @pytest.mark.parametrize("la,lb", LAYOUTS)
 def test_every_schedule_variant_bit_exact(sched, dtl, waves, la, lb):
-    if dtl and (la, lb) == ("col", "row"):
+    if dtl == 1 and (la, lb) == ("col", "row"):
         pytest.skip("no K-contiguous operand to load directly")
+    if dtl == 2 and (la, lb) == ("row", "col"):
+        pytest.skip("no transposed operand")
     from helpers import env
     M, N, K = 264, 520, 456
     _say("sched", sched, dtl, waves, la, lb)
     inp = _inputs_int(M, N, K, la, lb, "f16", seed=97)
     with env(DGEMM_FORCE_SCHED=sched, DGEMM_FORCE_DTL=dtl, DGEMM_FORCE_WAVES=waves):
         c, info = run_gpu(inp, "f16", "f32", split_k=1, force_tile="256x256", guard=16)
-    assert info["waves"] == waves and (info["direct_lds"] != 0) == bool(dtl)
+    assert info["waves"] == waves and info["schedule"] == sched
+    assert (info["direct_lds"] != 0) == bool(dtl) and ((info["direct_lds"] & 12) != 0) == (dtl == 2)
     _, ref = reference(inp, "f16", "f32")
     assert np.array_equal(c, ref)
 
@@ -358,40 +364,53 @@ def _tr_bits(la, lb):
     return ((1 if la == "row" else 4) | (2 if lb == "col" else 8))
 
 
+def _tr_sched_instantiated(fmt, la, lb, sched):
+    # ping-pong with transposing reads: every layout for fp16, NT only for bf16
+    return sched == 0 or fmt == "f16" or (la, lb) == ("col", "row")
+
+
 @pytest.mark.parametrize("la,lb", TR_LAYOUTS)
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
-def test_transposing_lds_reads_integer_bit_exact(la, lb, fmt):
+@pytest.mark.parametrize("sched", [1, 0])
+def test_transposing_lds_reads_integer_bit_exact(la, lb, fmt, sched):
     # transposed operands kept in global order in padded, K-row-permuted LDS blocks and
-    # transposed by ds_read_b64_tr_b16; ragged M, N and K
+    # transposed by ds_read_b64_tr_b16, in the ping-pong (1) and the pipeline (0) schedule;
+    # ragged M, N and K
+    if not _tr_sched_instantiated(fmt, la, lb, sched):
+        pytest.skip("not instantiated")
     from helpers import env
     M, N, K = 392 + 8, 648, 200
-    _say("tr-int", la, lb, fmt)
+    _say("tr-int", la, lb, fmt, sched)
     inp = _inputs_int(M, N, K, la, lb, fmt, seed=101)
-    with env(DGEMM_FORCE_DTL=2):
+    with env(DGEMM_FORCE_DTL=2, DGEMM_FORCE_SCHED=sched):
         c, info = run_gpu(inp, fmt, "f32", split_k=1, force_tile="256x256", guard=64)
-    assert info["direct_lds"] == _tr_bits(la, lb)
+    assert info["direct_lds"] == _tr_bits(la, lb) and info["schedule"] == sched
     assert (info["perm_block"], info["perm_stride"], info["lds_pad_bytes"]) == (8, 4, 64)
     _, ref = reference(inp, fmt, "f32")
     assert np.array_equal(c, ref)
 
 
 @pytest.mark.parametrize("la,lb", TR_LAYOUTS)
-def test_transposing_lds_reads_split_k_and_random(la, lb):
+@pytest.mark.parametrize("sched", [1, 0])
+def test_transposing_lds_reads_split_k_and_random(la, lb, sched):
     from helpers import env
     M, N, K = 264, 520, 1032
-    _say("tr-split", la, lb)
+    _say("tr-split", la, lb, sched)
     inp = _inputs_int(M, N, K, la, lb, "f16", seed=103)
     _, ref = reference(inp, "f16", "f32")
-    with env(DGEMM_FORCE_DTL=2):
+    with env(DGEMM_FORCE_DTL=2, DGEMM_FORCE_SCHED=sched):
         for sk in (1, 4):
             c, info = run_gpu(inp, "f16", "f32", split_k=sk, force_tile="256x256", guard=16)
             assert info["direct_lds"] == _tr_bits(la, lb) and info["split_k"] == sk
+            assert info["schedule"] == sched
             assert np.array_equal(c, ref), sk
-        inp = _inputs_rand(520, 392, 328, la, lb, "bf16", seed=105)
-        c, _ = run_gpu(inp, "bf16", "bf16", split_k=1, force_tile="256x256", guard=16)
-    _, ref = reference(inp, "bf16", "bf16")
-    amax, bmax = operand_max(inp, "bf16")
-    check_tolerance(c, ref, "bf16", 328, amax, bmax, "tr")
+        fmt = "bf16" if _tr_sched_instantiated("bf16", la, lb, sched) else "f16"
+        inp = _inputs_rand(520, 392, 328, la, lb, fmt, seed=105)
+        c, info = run_gpu(inp, fmt, fmt, split_k=1, force_tile="256x256", guard=16)
+        assert info["schedule"] == sched
+    _, ref = reference(inp, fmt, fmt)
+    amax, bmax = operand_max(inp, fmt)
+    check_tolerance(c, ref, fmt, 328, amax, bmax, "tr")
 
 
 @pytest.mark.parametrize("v,M", [("4x16x2", 5), ("2x8x4", 5), ("8x8x2", 16), ("tile", 384)])
@@ -446,7 +465,7 @@ def test_int4_256_tiles_both_schedules_bit_exact(sched, tiled, sk):
 
 @pytest.mark.parametrize("M,N,K", [(8, 8, 16), (24, 40, 8), (264, 8, 72), (8, 520, 136)])
 @pytest.mark.parametrize("la,lb", LAYOUTS)
-@pytest.mark.parametrize("dtl,sched", [(1, 1), (1, 0), (2, 0)])
+@pytest.mark.parametrize("dtl,sched", [(1, 1), (1, 0), (2, 1), (2, 0)])
 def test_direct_to_lds_mostly_out_of_range_tiles(M, N, K, la, lb, dtl, sched):
     # one 256x256 tile almost entirely past M, N or K: the out-of-range direct-to-LDS loads
     # must leave zeros (or be ignored) and the partial steps must add nothing
@@ -459,6 +478,6 @@ def test_direct_to_lds_mostly_out_of_range_tiles(M, N, K, la, lb, dtl, sched):
     inp = _inputs_int(M, N, K, la, lb, "f16", seed=151)
     with env(DGEMM_FORCE_DTL=dtl, DGEMM_FORCE_SCHED=sched):
         c, info = run_gpu(inp, "f16", "f32", split_k=1, force_tile="256x256", guard=32)
-    assert info["direct_lds"] != 0
+    assert info["direct_lds"] != 0 and info["schedule"] == sched
     _, ref = reference(inp, "f16", "f32")
     assert np.array_equal(c, ref)
