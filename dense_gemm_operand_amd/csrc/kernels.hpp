@@ -17,10 +17,12 @@
 //   3. LDS stores into padded, row-permuted, K-contiguous tiles (lds_layout.hpp).
 //   4. 128-bit LDS reads of matrix-core fragments, v_mfma_f32_32x32x16_{f16,bf16} or
 //      v_mfma_f32_32x32x64_f8f6f4. Two LDS stages, register loads two steps ahead,
-//      direct-to-LDS loads one step ahead, one barrier per step (or, for two transposed
-//      16-bit operands, a ping-pong of two wave groups). Optionally a transposed operand also
-//      goes straight into LDS in global order and is transposed by ds_read_b64_tr_b16
-//      (rocm-libraries PR 2487's direct-to-LDS layout with padding and row permutation).
+//      direct-to-LDS loads one step ahead. Main loop: two wave groups in ping-pong (one
+//      multiplies while the other reads LDS, stores and loads; a fenced barrier after every
+//      phase), or a software pipeline with one barrier per step. A transposed 16-bit operand
+//      can also go straight into LDS in global order and be transposed by ds_read_b64_tr_b16
+//      (rocm-libraries PR 2487's direct-to-LDS layout with padding and row permutation); the
+//      planner takes that loader when both operands are transposed.
 //   5. Split-K across workgroups (BitBLAS PR 268, "SplitK Infer"; the K origin of split
 //      z is z * k_chunk): each split stores its fp32 partial tile; the last split to
 //      arrive at the tile's counter adds all partials in ascending split order.
