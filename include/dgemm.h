@@ -6,7 +6,9 @@
  * index is not the contiguous one (a "non-TN" operand: Triton PR 5223, "Feature
  * description", where such operands are called K-major / non-KContig) is read with
  * 128-bit coalesced loads, transposed in registers and stored K-contiguous in LDS, so
- * the matrix-core loop always reads K-contiguous fragments. Skinny shapes split K
+ * the matrix-core loop reads K-contiguous fragments (when both operands are transposed,
+ * they instead stay in global order in LDS and the LDS reads transpose them; see
+ * gemm_plan). Skinny shapes split K
  * (BitBLAS PR 268, "SplitK Infer") and reduce the partial sums first across the
  * wavefronts of a workgroup through LDS (IREE PR 19596, inter-subgroup reduction
  * description), then across workgroups. B may instead be 4-bit weight codes with
