@@ -15,6 +15,9 @@ under "workloads".
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only-headline]
        python bench.py --copy-probe   (plain device copy of known size, for scaling
                                        rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
+       python bench.py --vendor-pair [--layout-a row|col --layout-b row|col] [--steps K]
+                      (the 4096^3 fp16 GEMM, K calls of torch.mm (hipBLASLt) then K of this
+                       library on the same operand bytes: for side-by-side rocprofv3 counters)
        python bench.py --workload NAME [--layout-a row|col --layout-b row|col] [--steps K]
                       (only that workload, K launches: the target of per-workload profiles;
                        for the attention workload --layout-a gives the dtype, f16 or bf16)
@@ -306,6 +309,19 @@ def loader_comparison(rounds: int = 5, calls: int = 20) -> list:
     return res
 
 
+def _vendor_mm(h: "Gemm"):
+    """torch.mm (hipBLASLt on ROCm) on the operand bytes of a planned fp16 GEMM, as a callable.
+    The library's layouts as torch views of the same bytes: "row" A is [M][K], "col" A is
+    [K][M]; "col" B is [N][K], "row" B is [K][N]."""
+    import torch
+    A, B, _ = h.sets[0]
+    M, N, K = h.M, h.N, h.K
+    ta = A.view(torch.float16).view(M, K) if h.la == "row" else A.view(torch.float16).view(K, M).t()
+    tb = B.view(torch.float16).view(N, K).t() if h.lb == "col" else B.view(torch.float16).view(K, N)
+    out = torch.empty(M, N, dtype=torch.float16, device="cuda")
+    return lambda: torch.mm(ta, tb, out=out)
+
+
 def vendor_blas_comparison(rounds: int = 5, calls: int = 20) -> list:
     """Context, not a result: the 4096^3 fp16 GEMM of this library against torch.mm
     (which dispatches to the vendor hipBLASLt kernels on ROCm) on the same operand memory
@@ -318,14 +334,7 @@ def vendor_blas_comparison(rounds: int = 5, calls: int = 20) -> list:
     res = []
     for la, lb in [("col", "col"), ("row", "col"), ("row", "row"), ("col", "row")]:
         h = Gemm(wl, la, lb)
-        A, B, _ = h.sets[0]
-        M, N, K = h.M, h.N, h.K
-        # the library's layouts as torch views of the same bytes: "row" A is [M][K], "col" A
-        # is [K][M]; "col" B is [N][K], "row" B is [K][N]
-        ta = A.view(torch.float16).view(M, K) if la == "row" else A.view(torch.float16).view(K, M).t()
-        tb = B.view(torch.float16).view(N, K).t() if lb == "col" else B.view(torch.float16).view(K, N)
-        out = torch.empty(M, N, dtype=torch.float16, device="cuda")
-        runs = [h.run, lambda: torch.mm(ta, tb, out=out)]
+        runs = [h.run, _vendor_mm(h)]
         t = [[], []]
         for _ in range(rounds):
             for i, fn in enumerate(runs):
@@ -346,7 +355,7 @@ def vendor_blas_comparison(rounds: int = 5, calls: int = 20) -> list:
         log(json.dumps(rec))
         res.append(rec)
         h.close()
-        del h, ta, tb, out
+        del h, runs
         torch.cuda.empty_cache()
     # fp8 E4M3: torch._scaled_mm (hipBLASLt, unit scales) takes B column-major only (TN)
     wl8 = synth.WORKLOADS["square_4096_f8"]
@@ -451,6 +460,23 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": n}))
 
 
+def vendor_pair(la: str | None, lb: str | None, calls: int):
+    """`calls` launches of the vendor library's product, then `calls` of this library's, on
+    the same operand memory of the 4096^3 fp16 GEMM (one layout pair, default TN)."""
+    import torch
+    from dense_gemm_operand_amd import synth
+    h = Gemm(synth.WORKLOADS["square_4096"], la or "row", lb or "col")
+    mm = _vendor_mm(h)
+    for _ in range(calls):
+        mm()
+    torch.cuda.synchronize()
+    for _ in range(calls):
+        h.run()
+    torch.cuda.synchronize()
+    print(json.dumps({"vendor_pair": f"{h.la}/{h.lb}", "calls": calls}))
+    h.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -459,6 +485,7 @@ def main():
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--vendor-pair", action="store_true")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--layout-a", default=None)
     ap.add_argument("--layout-b", default=None)
@@ -470,6 +497,9 @@ def main():
     import torch
     if args.copy_probe:
         copy_probe()
+        return
+    if args.vendor_pair:
+        vendor_pair(args.layout_a, args.layout_b, args.steps)
         return
     if args.workload:
         run_workload(args.workload, args.layout_a, args.layout_b, args.steps)
