@@ -185,6 +185,32 @@ def test_headline_plans(fake_cus):
     assert (i["tile_m"], i["tile_n"], i["grid_x"]) == (192, 320, 255)   # non-power-of-2 tile
 
 
+@pytest.mark.parametrize("dt", [F16, BF16])
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 4096), (3072, 5120, 6144), (8192, 8192, 520)])
+def test_default_loader_and_schedule_per_layout(fake_cus, dt, M, N, K):
+    # every layout runs the ping-pong schedule on 256x256 tiles; K-contiguous operands go
+    # straight into LDS; a transposed operand is transposed in registers (64-row stride-8
+    # permuted rows) unless both are transposed (NT), where both go straight into LDS in
+    # global order and the LDS reads transpose them (blocks of 8 K rows, stride 4, 64 B pad)
+    want = {(ROW, COL): (3, (1, 1), 0), (COL, COL): (2, (64, 8), 16), (ROW, ROW): (1, (64, 8), 16),
+            (COL, ROW): (12, (8, 4), 64)}
+    for (la, lb), (bits, perm, pad) in want.items():
+        p = dg.gemm_plan(M, N, K, la, lb, dt, dt, dt, 1)
+        i = dg.gemm_plan_query(p)
+        dg.gemm_plan_destroy(p)
+        assert (i["tile_m"], i["tile_n"], i["waves"], i["schedule"]) == (256, 256, 8, 1), (la, lb)
+        assert i["direct_lds"] == bits, (la, lb)
+        assert (i["perm_block"], i["perm_stride"]) == perm, (la, lb)
+        assert i["lds_pad_bytes"] == pad, (la, lb)
+        assert i["lds_bytes"] <= 160 * 1024
+    # the in-register transpose stays selectable for NT
+    with env(DGEMM_FORCE_DTL=0):
+        p = dg.gemm_plan(M, N, K, COL, ROW, dt, dt, dt, 1)
+        i = dg.gemm_plan_query(p)
+        dg.gemm_plan_destroy(p)
+    assert (i["direct_lds"], i["schedule"], i["perm_block"]) == (0, 1, 64)
+
+
 def test_lds_row_permutation_matches_the_page_formula():
     for B in range(1, 257):
         for S in range(1, B + 1):
