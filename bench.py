@@ -41,22 +41,27 @@ PEAK_F8_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak
 PEAK_GBS = 8000.0         # MI355X HBM3E
 MALL_BYTES = 256 << 20    # Infinity Cache: HBM-bound timings rotate over more than 2x this
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_square_4096_nn.txt")
-KERNEL_SRC = os.path.join(ROOT, "dense_gemm_operand_amd", "csrc", "kernels.hpp")
+KERNEL_DIR = os.path.join(ROOT, "dense_gemm_operand_amd", "csrc")
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_sha(path: str = KERNEL_SRC) -> str:
-    """Hash of a kernel source with comments and blank lines removed: counters taken on a
-    build stay valid across comment edits, and become stale when any code line changes."""
+def kernel_sha(folder: str = KERNEL_DIR) -> str:
+    """Hash of the device-code sources (every .hpp and .hip under csrc, in name order) with
+    comments and blank lines removed: counters taken on a build stay valid across comment
+    edits, and become stale when any code line of any kernel changes."""
     code = []
-    with open(path, encoding="utf-8") as f:
-        for ln in f:
-            ln = ln.split("//", 1)[0].rstrip()
-            if ln:
-                code.append(ln)
+    for name in sorted(os.listdir(folder)):
+        if not name.endswith((".hpp", ".hip")):
+            continue
+        code.append("== " + name)
+        with open(os.path.join(folder, name), encoding="utf-8") as f:
+            for ln in f:
+                ln = ln.split("//", 1)[0].rstrip()
+                if ln:
+                    code.append(ln)
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
@@ -125,21 +130,25 @@ class Gemm:
         self.i += 1
         self.dg.gemm_run(self.plan, A, B, S, self.C, self.ws)
 
-    def time_events(self, n: int, warm: int = 10) -> float:
-        """Average launch duration in ms from HIP event pairs on the launch stream."""
+    def time_b2b(self, n: int, warm: int = 10) -> float:
+        """Average launch duration in ms: `n` back-to-back launches on the launch stream
+        bracketed by one HIP event pair (the same way the headline's timed region is taken).
+        Kernels shorter than 50 us are timed with time_graph instead, so that the host's
+        enqueue rate cannot enter the figure."""
         torch = self.torch
         for _ in range(warm):
             self.run()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(n)]
         torch.cuda.synchronize()
-        for s, e in ev:
-            s.record()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
             self.run()
-            e.record()
+        e1.record()
         torch.cuda.synchronize()
-        d = sorted(s.elapsed_time(e) for s, e in ev)
-        return float(np.mean(d)), float(d[len(d) // 2]), float(d[0])
+        ms = e0.elapsed_time(e1) / n
+        if ms < 0.05 and hasattr(self, "time_graph"):
+            ms = self.time_graph()
+        return ms
 
     def time_graph(self, launches: int = 32, replays: int = 10):
         """Average launch duration in ms for kernels too short for per-launch events: a
@@ -192,7 +201,7 @@ class Attn:
     def run(self):
         self.dg.attn_fwd(*self.args)
 
-    time_events = Gemm.time_events
+    time_b2b = Gemm.time_b2b
 
 
 def cpu_baseline(g: Gemm, budget_s: float = 12.0):
@@ -261,45 +270,53 @@ def stream_context() -> dict:
             "note": "torch sum over 2 GiB fp16 and copy of 1 GiB, events over 5 runs each"}
 
 
+def interleaved(fns, rounds: int = 5, calls: int = 20) -> list:
+    """Median ms per call of each callable, timed interleaved: rounds of `calls`
+    back-to-back calls per callable, alternating, one event pair per batch, so that the
+    power-limited clock affects every callable alike."""
+    import torch
+    t = [[] for _ in fns]
+    for _ in range(rounds):
+        for i, fn in enumerate(fns):
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(calls):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t[i].append(e0.elapsed_time(e1) / calls)
+    return [float(np.median(x)) for x in t]
+
+
 def loader_comparison(rounds: int = 5, calls: int = 20) -> list:
-    """The two loaders for transposed operands on the same shapes, timed interleaved
-    (rounds of `calls` back-to-back launches, alternating) so that clock drift on the box
-    affects both alike: the in-register transpose (the default where one operand is
-    K-contiguous; planner hook DGEMM_FORCE_DTL=0 where none is) and direct-to-LDS loads in
-    global order transposed by the LDS reads (DGEMM_FORCE_DTL=2; the default for NT)."""
+    """The two loaders for transposed operands on the same shapes, timed interleaved: the
+    in-register transpose (the default where one operand is K-contiguous; planner hook
+    DGEMM_FORCE_DTL=0 where none is) and direct-to-LDS loads in global order transposed by
+    the LDS reads (DGEMM_FORCE_DTL=2; the default for NT). The default kernel's own time is
+    the one under "workloads"; here only the alternative's time and the ratio appear."""
     import torch
     from dense_gemm_operand_amd import synth
     res = []
     for name, la, lb in [("square_4096", "col", "col"), ("square_4096", "row", "row"),
                          ("square_4096", "col", "row"), ("nonpow2_bf16", None, None)]:
         wl = synth.WORKLOADS[name]
-        hs = []
         nt = (la or wl.layout_a) == "col" and (lb or wl.layout_b) == "row"
-        for dtl in ("0" if nt else None, "2"):
+        hs = []
+        for dtl in (None, "2" if not nt else "0"):   # default first, then the other loader
             if dtl is not None:
                 os.environ["DGEMM_FORCE_DTL"] = dtl
             try:
                 hs.append(Gemm(wl, la, lb))
             finally:
                 os.environ.pop("DGEMM_FORCE_DTL", None)
-        t = [[], []]
-        for _ in range(rounds):
-            for i, h in enumerate(hs):
-                for _ in range(3):
-                    h.run()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                for _ in range(calls):
-                    h.run()
-                e1.record()
-                torch.cuda.synchronize()
-                t[i].append(e0.elapsed_time(e1) * 1e3 / calls)
-        rec = {"workload": name, "layout_a": hs[0].la, "layout_b": hs[0].lb}
-        for key, h, ts in (("in_register_transpose", hs[0], t[0]), ("transposing_lds_reads", hs[1], t[1])):
-            med = float(np.median(ts))
-            rec[key] = {"us_median": round(med, 2), "tflops": round(h.flops / (med * 1e-6) / 1e12, 1),
-                        "waves": h.info["waves"], "direct_lds": h.info["direct_lds"],
-                        "tile": f"{h.info['tile_m']}x{h.info['tile_n']}"}
+        d, alt = interleaved([hs[0].run, hs[1].run], rounds, calls)
+        loader = lambda h: "transposing_lds_reads" if h.info["direct_lds"] & 12 else "in_register_transpose"
+        rec = {"workload": name, "layout_a": hs[0].la, "layout_b": hs[0].lb,
+               "default": loader(hs[0]), "alternative": loader(hs[1]),
+               "alternative_us": round(alt * 1e3, 2),
+               "alternative_over_default": round(alt / d, 4)}
         log(json.dumps(rec))
         res.append(rec)
         for h in hs:
@@ -323,41 +340,25 @@ def _vendor_mm(h: "Gemm"):
 
 
 def vendor_blas_comparison(rounds: int = 5, calls: int = 20) -> list:
-    """Context, not a result: the 4096^3 fp16 GEMM of this library against torch.mm
-    (which dispatches to the vendor hipBLASLt kernels on ROCm) on the same operand memory
-    in each layout, and the fp8 E4M3 one against torch._scaled_mm in the layout it takes
-    (TN), timed interleaved (rounds of `calls` back-to-back launches) so that the
-    power-limited clock affects both alike."""
+    """Context, not a result: torch.mm (which dispatches to the vendor hipBLASLt kernels on
+    ROCm) on the same operand memory as the 4096^3 fp16 GEMM in each layout, and
+    torch._scaled_mm against the fp8 E4M3 one in the layout it takes (TN), timed
+    interleaved with this library. This library's own times are under "workloads"; here
+    the vendor's time and the ratio vendor / this library."""
     import torch
     from dense_gemm_operand_amd import synth
     wl = synth.WORKLOADS["square_4096"]
     res = []
     for la, lb in [("col", "col"), ("row", "col"), ("row", "row"), ("col", "row")]:
         h = Gemm(wl, la, lb)
-        runs = [h.run, _vendor_mm(h)]
-        t = [[], []]
-        for _ in range(rounds):
-            for i, fn in enumerate(runs):
-                for _ in range(3):
-                    fn()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                for _ in range(calls):
-                    fn()
-                e1.record()
-                torch.cuda.synchronize()
-                t[i].append(e0.elapsed_time(e1) * 1e3 / calls)
-        ours, blas = float(np.median(t[0])), float(np.median(t[1]))
+        ours, blas = interleaved([h.run, _vendor_mm(h)], rounds, calls)
         rec = {"workload": wl.name, "layout_a": la, "layout_b": lb,
-               "this_library_us": round(ours, 2), "torch_mm_us": round(blas, 2),
-               "this_library_tflops": round(h.flops / (ours * 1e-6) / 1e12, 1),
-               "torch_mm_tflops": round(h.flops / (blas * 1e-6) / 1e12, 1)}
+               "torch_mm_us": round(blas * 1e3, 2), "torch_mm_over_this": round(blas / ours, 4)}
         log(json.dumps(rec))
         res.append(rec)
         h.close()
-        del h, runs
+        del h
         torch.cuda.empty_cache()
-    # fp8 E4M3: torch._scaled_mm (hipBLASLt, unit scales) takes B column-major only (TN)
     wl8 = synth.WORKLOADS["square_4096_f8"]
     h = Gemm(wl8, "row", "col")
     A, B, _ = h.sets[0]
@@ -365,24 +366,11 @@ def vendor_blas_comparison(rounds: int = 5, calls: int = 20) -> list:
     ta = A.view(f8).view(h.M, h.K)
     tb = B.view(f8).view(h.N, h.K).t()
     one = torch.tensor(1.0, device="cuda")
-    runs = [h.run, lambda: torch._scaled_mm(ta, tb, scale_a=one, scale_b=one, out_dtype=torch.float16)]
-    t = [[], []]
-    for _ in range(rounds):
-        for i, fn in enumerate(runs):
-            for _ in range(3):
-                fn()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(calls):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            t[i].append(e0.elapsed_time(e1) * 1e3 / calls)
-    ours, blas = float(np.median(t[0])), float(np.median(t[1]))
+    ours, blas = interleaved([h.run, lambda: torch._scaled_mm(ta, tb, scale_a=one, scale_b=one,
+                                                              out_dtype=torch.float16)],
+                             rounds, calls)
     rec = {"workload": wl8.name, "layout_a": "row", "layout_b": "col",
-           "this_library_us": round(ours, 2), "torch_scaled_mm_us": round(blas, 2),
-           "this_library_tflops": round(h.flops / (ours * 1e-6) / 1e12, 1),
-           "torch_scaled_mm_tflops": round(h.flops / (blas * 1e-6) / 1e12, 1)}
+           "torch_scaled_mm_us": round(blas * 1e3, 2), "torch_scaled_mm_over_this": round(blas / ours, 4)}
     log(json.dumps(rec))
     res.append(rec)
     h.close()
@@ -392,9 +380,10 @@ def vendor_blas_comparison(rounds: int = 5, calls: int = 20) -> list:
 
 
 def int4_layout_comparison(rounds: int = 5) -> list:
-    """int4 B in the column-major packing and pre-tiled (64 columns x 128 K blocks), timed
-    interleaved: HIP graphs of back-to-back launches over rotating input sets for M = 16,
-    events over back-to-back launches for M = 4096."""
+    """int4 B pre-tiled (64 columns x 128 K blocks) against the column-major packing (the
+    workload's own layout, timed under "workloads"), interleaved: HIP graphs of
+    back-to-back launches over rotating input sets for M = 16, back-to-back launches for
+    M = 4096. Reports the pre-tiled time and the ratio."""
     import torch
     from dense_gemm_operand_amd import synth
     res = []
@@ -403,22 +392,66 @@ def int4_layout_comparison(rounds: int = 5) -> list:
         hbm = name == "int4_m16"
         rot = 2 * MALL_BYTES + (64 << 20) if hbm else 0
         hs = [Gemm(wl, rotate_bytes=rot), Gemm(wl, rotate_bytes=rot, b_tiled=True)]
-        t = [[], []]
-        for _ in range(rounds):
-            for i, h in enumerate(hs):
-                t[i].append(h.time_graph(32, 5) if hbm else h.time_events(10, 3)[1])
-        rec = {"workload": name, "M": hs[0].M, "N": hs[0].N, "K": hs[0].K}
-        for key, h, ts in (("column_major_codes", hs[0], t[0]), ("pre_tiled_codes", hs[1], t[1])):
-            med = float(np.median(ts))
-            rec[key] = {"us_median": round(med * 1e3, 2), "gbs": round(h.bytes / (med * 1e-3) / 1e9, 1),
-                        "tflops": round(h.flops / (med * 1e-3) / 1e12, 1), "split_k": h.info["split_k"],
-                        "tile": f"{h.info['tile_m']}x{h.info['tile_n']}"}
+        if hbm:
+            t = [[], []]
+            for _ in range(rounds):
+                for i, h in enumerate(hs):
+                    t[i].append(h.time_graph(32, 5))
+            col, tiled = float(np.median(t[0])), float(np.median(t[1]))
+        else:
+            col, tiled = interleaved([hs[0].run, hs[1].run], rounds, 10)
+        h = hs[1]
+        rec = {"workload": name, "M": h.M, "N": h.N, "K": h.K,
+               "pre_tiled_us": round(tiled * 1e3, 2),
+               "pre_tiled_gbs": round(h.bytes / (tiled * 1e-3) / 1e9, 1),
+               "pre_tiled_tflops": round(h.flops / (tiled * 1e-3) / 1e12, 1),
+               "pre_tiled_over_column_major": round(tiled / col, 4),
+               "split_k": h.info["split_k"], "tile": f"{h.info['tile_m']}x{h.info['tile_n']}"}
         log(json.dumps(rec))
         res.append(rec)
         for h in hs:
             h.close()
         del hs
         torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baselines(budget_s: float = 2.5) -> list:
+    """The oracle (untuned, all host threads) on a bounded sample of every workload and
+    layout: whole output rows, sized so that each takes about `budget_s` seconds including
+    the decode (and int4 dequant) of the operands. A reported baseline, not a target."""
+    import oracle
+    from dense_gemm_operand_amd import synth
+    res = []
+    cases = [("square_tt_256", None, None)] + \
+        [("square_4096", la, lb) for la, lb in synth.LAYOUT_LETTERS.values()] + \
+        [("nonpow2_bf16", None, None), ("skinny_splitk", None, None), ("int4_m16", None, None),
+         ("int4_m4096", None, None), ("square_4096_f8", None, None)]
+    for name, la, lb in cases:
+        w = synth.WORKLOADS[name]
+        inp = synth.make_inputs(w, layout_a=la, layout_b=lb)
+        M, N, K = inp["M"], inp["N"], inp["K"]
+        t0 = time.time()
+        a = oracle.operand_a(inp["A"], M, K, inp["layout_a"], w.dtype_ab)
+        b = oracle.operand_b(inp["B"], K, N, inp["layout_b"], "u4" if w.int4 else w.dtype_ab,
+                             inp.get("scales"))
+        prep = time.time() - t0
+        probe = min(M, max(1, oracle.threads()))
+        t1 = time.time()
+        oracle.gemm_f64(a, b, (0, probe))
+        per_row = max((time.time() - t1) / probe, 1e-7)
+        rows = int(max(1, min(M, (budget_s - prep) / per_row)))
+        t2 = time.time()
+        oracle.gemm_f64(a, b, (0, rows))
+        dt = time.time() - t2 + prep
+        flops = 2.0 * rows * N * K
+        rec = {"workload": name, "layout_a": inp["layout_a"], "layout_b": inp["layout_b"],
+               "M": M, "N": N, "K": K, "rows": rows, "seconds": round(dt, 3),
+               "gmacs": round(flops / 2 / dt / 1e9, 3), "tflops": round(flops / dt / 1e12, 6),
+               "cores": oracle.threads(), "kind": "oracle"}
+        log(json.dumps(rec))
+        res.append(rec)
+        del a, b, inp
     return res
 
 
@@ -512,17 +545,22 @@ def main():
     for _ in range(args.warmup):
         g.run()
     torch.cuda.synchronize()
+    # The timed region: K back-to-back launches on the launch stream (torch's current
+    # stream), bracketed by a host clock and by one HIP event pair on that stream.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record()
     for _ in range(args.steps):
         g.run()
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     value = g.flops / (ms_step * 1e-3) / 1e12
-    avg_ms, med_ms, min_ms = g.time_events(max(args.steps, 50))
-    achieved = g.flops / (avg_ms * 1e-3) / 1e12
-    log(f"headline: wall {ms_step * 1e3:.1f} us/step, event avg {avg_ms * 1e3:.1f} us "
-        f"(median {med_ms * 1e3:.1f}, min {min_ms * 1e3:.1f}) -> {achieved:.1f} TFLOP/s")
+    kern_ms = e0.elapsed_time(e1) / args.steps
+    achieved = g.flops / (kern_ms * 1e-3) / 1e12
+    log(f"headline: wall {ms_step * 1e3:.1f} us/step, events over the same region "
+        f"{kern_ms * 1e3:.1f} us/launch -> {achieved:.1f} TFLOP/s")
 
     out = {
         "metric": "TFLOP/s and % of dense MFMA peak, 4096^3 NN fp16 GEMM; GB/s for split-K",
@@ -541,15 +579,17 @@ def main():
                                "K-contiguous), fp32 accumulate, fp16 out, N(0,1)/sqrt(K)",
                    "M": 4096, "N": 4096, "K": 4096, "layout_a": "col", "layout_b": "col",
                    "tile": f"{g.info['tile_m']}x{g.info['tile_n']}x{g.info['tile_k']}",
-                   "split_k": g.info["split_k"]},
+                   "waves": g.info["waves"], "split_k": g.info["split_k"]},
         "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2),
     }
     traffic = read_traffic()
     out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                        "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
                        "traffic": traffic,
-                       "kernel_avg_us": round(avg_ms * 1e3, 2),
-                       "flops_per_launch": g.flops}
+                       "kernel_avg_us": round(kern_ms * 1e3, 2),
+                       "flops_per_launch": g.flops,
+                       "timing": "HIP events on the launch stream around the timed region, "
+                                 "divided by the launches in it"}
     if not args.no_cpu:
         out["cpu_baseline"], out["parity_spot_check"] = cpu_baseline(g)
     g.close()
@@ -558,33 +598,26 @@ def main():
 
     if not args.only_headline:
         extra = []
-        # (workload, layouts, bound, planner hooks)
+        # (workload, layouts, bound); the headline NN layout is timed above
         cases = [
-            ("square_4096", "row", "row", "mfma", {}), ("square_4096", "col", "row", "mfma", {}),
-            ("square_4096", "row", "col", "mfma", {}), ("nonpow2_bf16", None, None, "mfma", {}),
-            ("square_tt_256", None, None, "mfma", {}), ("int4_m4096", None, None, "mfma", {}),
-            ("skinny_splitk", None, None, "hbm", {}), ("int4_m16", None, None, "hbm", {}),
-            ("square_4096_f8", None, None, "mfma", {}), ("square_4096_f8", "row", "col", "mfma", {}),
+            ("square_4096", "row", "row", "mfma"), ("square_4096", "col", "row", "mfma"),
+            ("square_4096", "row", "col", "mfma"), ("nonpow2_bf16", None, None, "mfma"),
+            ("square_tt_256", None, None, "mfma"), ("int4_m4096", None, None, "mfma"),
+            ("skinny_splitk", None, None, "hbm"), ("int4_m16", None, None, "hbm"),
+            ("square_4096_f8", None, None, "mfma"), ("square_4096_f8", "row", "col", "mfma"),
         ]
-        for name, la, lb, bound, hooks in cases:
+        for name, la, lb, bound in cases:
             wl = synth.WORKLOADS[name]
             rot = 2 * MALL_BYTES + (64 << 20) if bound == "hbm" else 0
-            os.environ.update(hooks)
-            try:
-                h = Gemm(wl, la, lb, rotate_bytes=rot)
-            finally:
-                for k in hooks:
-                    os.environ.pop(k, None)
-            avg, med, mn = h.time_events(100 if bound == "hbm" else 50)
-            if avg < 0.1:   # short kernel: per-launch events would time the host enqueue gap
-                avg = med = mn = h.time_graph()
+            h = Gemm(wl, la, lb, rotate_bytes=rot)
+            ms = h.time_b2b(100 if bound == "hbm" else 50)
             rec = {"workload": name, "M": h.M, "N": h.N, "K": h.K, "layout_a": h.la,
                    "layout_b": h.lb, "dtype": wl.dtype_ab + ("+u4" if wl.int4 else ""),
                    "out": wl.dtype_c, "split_k": h.info["split_k"],
-                   "tile": f"{h.info['tile_m']}x{h.info['tile_n']}", "us_avg": round(avg * 1e3, 2),
-                   "us_median": round(med * 1e3, 2),
-                   "tflops": round(h.flops / (avg * 1e-3) / 1e12, 2),
-                   "gbs": round(h.bytes / (avg * 1e-3) / 1e9, 1),
+                   "tile": f"{h.info['tile_m']}x{h.info['tile_n']}", "kernel": h.info["kernel"],
+                   "us": round(ms * 1e3, 2),
+                   "tflops": round(h.flops / (ms * 1e-3) / 1e12, 2),
+                   "gbs": round(h.bytes / (ms * 1e-3) / 1e9, 1),
                    "input_sets": len(h.sets),
                    "loader": ("transposing LDS reads" if h.info["direct_lds"] & 12 else
                               "in-register transpose" if (h.la == "col" or h.lb == "row") else
@@ -602,22 +635,26 @@ def main():
         for dt in ("f16", "bf16"):
             aw = synth.ATTN_WORKLOADS["attn_4096"]
             at = Attn(aw, dt)
-            avg, med, mn = at.time_events(30, warm=5)
+            ms = at.time_b2b(30, warm=5)
             rec = {"workload": aw.name, "batch_heads": aw.BH, "seq_q": aw.seq_q, "seq_k": aw.seq_k,
-                   "head_dim": aw.head_dim, "dtype": dt, "us_avg": round(avg * 1e3, 2),
-                   "us_median": round(med * 1e3, 2),
-                   "tflops": round(at.flops / (avg * 1e-3) / 1e12, 2),
-                   "pct_peak": round(100 * at.flops / (avg * 1e-3) / 1e12 / PEAK_TFLOPS, 2),
+                   "head_dim": aw.head_dim, "dtype": dt, "us": round(ms * 1e3, 2),
+                   "tflops": round(at.flops / (ms * 1e-3) / 1e12, 2),
+                   "pct_peak": round(100 * at.flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS, 2),
                    "bound": "mfma", "loader": "V transposed in registers (attention P*V)"}
             log(json.dumps(rec))
             extra.append(rec)
             del at
             torch.cuda.empty_cache()
         out["workloads"] = extra
+        out["timing"] = ("every time above: back-to-back launches bracketed by one HIP event "
+                         "pair on the launch stream (HIP graph replays for kernels under 50 "
+                         "us); the comparisons below give ratios from interleaved batches")
         out["loader_comparison"] = loader_comparison()
         out["int4_layout_comparison"] = int4_layout_comparison()
         out["vendor_blas_comparison"] = vendor_blas_comparison()
         out["context"] = stream_context()
+        if not args.no_cpu:
+            out["cpu_baseline_per_workload"] = cpu_baselines()
     print(json.dumps(out), flush=True)
 
 

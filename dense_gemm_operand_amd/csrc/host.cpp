@@ -207,13 +207,10 @@ int make_plan(Plan& p, int split_k_req) {
     p.grid_y = sk;
     p.grid_z = 1;
   }
-  // fp32 partial tile as the kernels store it: every thread's accumulator vectors
-  // (tiled: the whole tile; skinny: the reduced tile spread over all threads).
-  int64_t per_tile = (int64_t)p.tile_m * p.tile_n * 4;
-  if (v.kernel == KERNEL_SKINNY) {
-    const int64_t threads = 64LL * v.waves, pos = (int64_t)(v.tile_n / 16) * 64;
-    per_tile = cdiv(pos, threads) * threads * 16;
-  }
+  // fp32 partial tile as the kernels store it: the whole tile (the tiled kernel's
+  // accumulators, the skinny kernel's reduced tile of 16 x tile_n fp32 values, which its
+  // threads own in whole four-value positions)
+  const int64_t per_tile = (int64_t)(v.kernel == KERNEL_SKINNY ? 16 : p.tile_m) * p.tile_n * 4;
   p.partial_bytes_per_split = tiles * per_tile;
   p.workspace_bytes = sk > 1 ? kCounterBytes + (int64_t)sk * p.partial_bytes_per_split : 0;
   if (debug_on())

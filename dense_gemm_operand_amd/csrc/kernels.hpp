@@ -221,32 +221,37 @@ struct KArgs {
   int zero;             // int4: zero point (0 .. 15)
 };
 
-// Split-K fix-up shared by both kernels. Every thread owns NV vectors of LEN fp32
-// partial sums; the workgroup stores them into split z's slot, the last workgroup to
-// arrive at the tile's counter adds all splits in ascending split order and returns
-// true; the others return false. The counter is reset for the next run.
+// Split-K fix-up shared by both kernels. Threads tid < LIVE own NV vectors of LEN fp32
+// partial sums (the others own nothing: the skinny kernel's reduced tile has fewer
+// positions than threads); the workgroup stores them into split z's slot, the last
+// workgroup to arrive at the tile's counter adds all splits in ascending split order and
+// returns true; the others return false. The counter is reset for the next run.
 //
 // Cross-XCD visibility without cache maintenance: partials are written and read with
 // agent-scope relaxed atomics (device-coherent stores and loads that go to the memory
 // side, past the XCD-private L2), every thread waits for its stores to complete before
 // the workgroup barrier, and only then is the counter incremented (agent scope). An
 // agent-scope release/acquire fence would instead write back and invalidate the whole
-// L2 of the XCD for every workgroup. Layout: element-major [split][tile][v][e][thread],
+// L2 of the XCD for every workgroup. Layout: element-major [split][tile][v][e][live thread],
 // so every store and load instruction covers consecutive addresses.
-template <class V, int NV, int THREADS>
+template <class V, int NV, int THREADS, int LIVE = THREADS>
 __device__ __forceinline__ bool splitk_fixup(V (&acc)[NV], const KArgs& a, int tile,
                                              int z, int sk, int tiles) {
   constexpr int LEN = sizeof(V) / sizeof(float);
+  static_assert(LIVE <= THREADS && (NV == 1 || LIVE == THREADS), "live threads");
   __shared__ int s_last;
   const int tid = threadIdx.x;
-  const size_t per_tile = (size_t)NV * LEN * THREADS;
+  const bool live = tid < LIVE;
+  const size_t per_tile = (size_t)NV * LEN * LIVE;
   float* mine = a.part + ((size_t)z * tiles + tile) * per_tile;
+  if (live) {
 #pragma unroll
-  for (int v = 0; v < NV; ++v)
+    for (int v = 0; v < NV; ++v)
 #pragma unroll
-    for (int e = 0; e < LEN; ++e)
-      __hip_atomic_store(mine + ((size_t)v * LEN + e) * THREADS + tid, acc[v][e], __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      for (int e = 0; e < LEN; ++e)
+        __hip_atomic_store(mine + ((size_t)v * LEN + e) * LIVE + tid, acc[v][e], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  }
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
   __syncthreads();
   if (tid == 0) {
@@ -258,17 +263,19 @@ __device__ __forceinline__ bool splitk_fixup(V (&acc)[NV], const KArgs& a, int t
   if (!s_last) return false;
   const float* base = a.part + (size_t)tile * per_tile;
   const size_t split_stride = (size_t)tiles * per_tile;
+  if (live) {
 #pragma unroll
-  for (int v = 0; v < NV; ++v) {
+    for (int v = 0; v < NV; ++v) {
 #pragma unroll
-    for (int e = 0; e < LEN; ++e) {
-      const size_t idx = ((size_t)v * LEN + e) * THREADS + tid;
-      float s = (z == 0) ? acc[v][e] : __hip_atomic_load(base + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      for (int b = 1; b < sk; ++b)
-        s += (b == z) ? acc[v][e]
-                      : __hip_atomic_load(base + b * split_stride + idx, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-      acc[v][e] = s;
+      for (int e = 0; e < LEN; ++e) {
+        const size_t idx = ((size_t)v * LEN + e) * LIVE + tid;
+        float s = (z == 0) ? acc[v][e] : __hip_atomic_load(base + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int b = 1; b < sk; ++b)
+          s += (b == z) ? acc[v][e]
+                        : __hip_atomic_load(base + b * split_stride + idx, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+        acc[v][e] = s;
+      }
     }
   }
   if (tid == 0)
@@ -1279,6 +1286,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
 // KI K indices: lane (r = lane%16, c = lane/16) loads, for B row n0+16*nb+r and A row r,
 // the K range [k + c*KI/4, k + (c+1)*KI/4); matrix-core step h uses the lane's h-th group
 // of eight K indices, identically for A and B, so the pairing of K indices is exact.
+// Iterations are dealt to the waves in turn (iteration i to wave i % W), so at any time the
+// workgroup reads one contiguous K window of every column.
+// Main loop: two register sets of U iterations each. While one set is multiplied, the
+// other set's loads are in flight, and each set is reloaded as soon as it has been used.
+// The loop body has no branches: an iteration past the split's end loads with
+// out-of-range offsets, which return zeros, and multiplies zeros. So the compiler can wait
+// for exactly the loads each multiply needs (it counts outstanding loads in issue order)
+// instead of for every outstanding load.
 template <class T, bool U4B, int NB, int W, int U>
 __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
   constexpr int THREADS = W * 64;
@@ -1293,21 +1308,22 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
   const int kb = z * a.k_chunk;
   const int ke = min(a.K, kb + a.k_chunk);
   const int n_it = ke > kb ? (ke - kb + KI - 1) / KI : 0;
-  const int my_n = n_it > wave ? (n_it - wave + W - 1) / W : 0;
 
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.A, a.bytesA);
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.B, a.bytesB);
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.S, a.bytesS);
 
   constexpr int BV = U4B ? 1 : H;      // 16-byte B vectors per lane per n-block
-  u32x4 bufA[U][H];
-  u32x4 bufB[U][NB][BV];
-  uint16_t bufS[U][NB];
+  u32x4 bufA[2][U][H];
+  u32x4 bufB[2][U][NB][BV];
+  uint16_t bufS[2][U][NB];
 
   // int4: every load of an iteration lies inside the split (split chunks are multiples of
   // 128 and K % 128 == 0) and rows past M or N start past the end of their buffer, where
   // buffer loads return zeros; so the offsets are per-lane constants plus a wave-uniform
-  // per-iteration term (scalar offset), with no per-load bounds arithmetic.
+  // per-iteration term (scalar offset), with no per-load bounds arithmetic. An iteration
+  // past the split's end takes the scalar offset kOOB: every per-lane offset is below 2^31,
+  // so the sum stays below 2^32 and lies past every buffer's end.
   uint32_t offA0 = 0, offB0[NB], offS0[NB];
   if constexpr (U4B) {
     offA0 = (uint32_t)(r * a.ldA + kb + c * KL) * 2u;
@@ -1324,34 +1340,37 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
     }
   }
   const uint32_t b_iter = a.b_tiled ? 4096u : (uint32_t)(KI / 2);   // B bytes per iteration
-  auto load = [&](int u, int j) {
-    const int it = wave + j * W;
+  // Loads of iteration `it` of this split into slot u of register set SET.
+  auto load = [&](auto SET_, int u, int it) {
+    constexpr int SET = decltype(SET_)::value;
+    const bool live = it < n_it;
     if constexpr (U4B) {
-      const uint32_t sa = (uint32_t)it * KI * 2u, sb = (uint32_t)it * b_iter;
-      const uint32_t ss = (uint32_t)((kb + it * KI) >> a.group_log2) * (uint32_t)a.N * 2u;
+      const uint32_t sa = live ? (uint32_t)it * KI * 2u : kOOB;
+      const uint32_t sb = live ? (uint32_t)it * b_iter : kOOB;
+      const uint32_t ss = live ? (uint32_t)((kb + it * KI) >> a.group_log2) * (uint32_t)a.N * 2u : kOOB;
 #pragma unroll
       for (int h = 0; h < H; ++h)
-        bufA[u][h] = __builtin_amdgcn_raw_buffer_load_b128(rA, offA0 + 16u * h, sa, 0);
+        bufA[SET][u][h] = __builtin_amdgcn_raw_buffer_load_b128(rA, offA0 + 16u * h, sa, 0);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        bufB[u][nb][0] = __builtin_amdgcn_raw_buffer_load_b128(rB, offB0[nb], sb, 0);
-        bufS[u][nb] = __builtin_amdgcn_raw_buffer_load_b16(rS, offS0[nb], ss, 0);
+        bufB[SET][u][nb][0] = __builtin_amdgcn_raw_buffer_load_b128(rB, offB0[nb], sb, 0);
+        bufS[SET][u][nb] = __builtin_amdgcn_raw_buffer_load_b16(rS, offS0[nb], ss, 0);
       }
       return;
     }
     const int k = kb + it * KI + c * KL;
 #pragma unroll
     for (int h = 0; h < H; ++h) {
-      const bool ok = r < a.M && k + 8 * h < ke;
-      bufA[u][h] = ld128(rA, ok ? (uint32_t)(r * a.ldA + k + 8 * h) * 2u : kOOB);
+      const bool ok = live && r < a.M && k + 8 * h < ke;
+      bufA[SET][u][h] = ld128(rA, ok ? (uint32_t)(r * a.ldA + k + 8 * h) * 2u : kOOB);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int n = n0 + 16 * nb + r;
 #pragma unroll
       for (int h = 0; h < H; ++h) {
-        const bool ok = n < a.N && k + 8 * h < ke;
-        bufB[u][nb][h] = ld128(rB, ok ? (uint32_t)(n * a.ldB + k + 8 * h) * 2u : kOOB);
+        const bool ok = live && n < a.N && k + 8 * h < ke;
+        bufB[SET][u][nb][h] = ld128(rB, ok ? (uint32_t)(n * a.ldB + k + 8 * h) * 2u : kOOB);
       }
     }
   };
@@ -1360,49 +1379,58 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int u) {
-    // int4: the activation fragments take the weights' K order (pairs k, k+4), once per
-    // iteration for all NB blocks
-    u32x4 ap[U4B ? H : 1];
+  const _Float16 zb = (_Float16)(-1024 - a.zero), zb16 = (_Float16)(-64 - a.zero);
+  const f16x2 bias = {zb, zb}, bias16 = {zb16, zb16};
+  auto compute = [&](auto SET_, int u) {
+    constexpr int SET = decltype(SET_)::value;
     if constexpr (U4B) {
+      // the activation fragments take the weights' K order (pairs k, k+4), once per
+      // iteration for all NB blocks
+      u32x4 ap[H];
 #pragma unroll
-      for (int h = 0; h < H; ++h) ap[h] = pair_k_and_k4(bufA[u][h]);
-    }
-    const _Float16 zb = (_Float16)(-1024 - a.zero), zb16 = (_Float16)(-64 - a.zero);
-    const f16x2 bias = {zb, zb}, bias16 = {zb16, zb16};
+      for (int h = 0; h < H; ++h) ap[h] = pair_k_and_k4(bufA[SET][u][h]);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      if constexpr (U4B) {
-        const _Float16 s = __builtin_bit_cast(_Float16, bufS[u][nb]);
-        const f16x2 s2 = {s, s};
+      for (int h = 0; h < H; ++h)
 #pragma unroll
-        for (int h = 0; h < H; ++h)
-          acc[nb] = mfma16x16x32<T>(dequant8_pairs(bufB[u][nb][0][h], s2, bias, bias16), ap[h], acc[nb]);
-      } else {
+        for (int nb = 0; nb < NB; ++nb) {
+          const _Float16 s = __builtin_bit_cast(_Float16, bufS[SET][u][nb]);
+          const f16x2 s2 = {s, s};
+          acc[nb] = mfma16x16x32<T>(dequant8_pairs(bufB[SET][u][nb][0][h], s2, bias, bias16), ap[h], acc[nb]);
+        }
+    } else {
 #pragma unroll
-        for (int h = 0; h < H; ++h)
-          acc[nb] = mfma16x16x32<T>(bufB[u][nb][h], bufA[u][h], acc[nb]);
-      }
+      for (int h = 0; h < H; ++h)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[nb] = mfma16x16x32<T>(bufB[SET][u][nb][h], bufA[SET][u][h], acc[nb]);
     }
   };
 
+  // iteration of slot u in round q (rounds of W*U iterations; round q uses set q % 2)
+  auto iter = [&](int q, int u) { return q * (W * U) + u * W + wave; };
+  const int rounds = (n_it + W * U - 1) / (W * U);
 #pragma unroll
-  for (int u = 0; u < U; ++u)
-    if (u < my_n) load(u, u);
-  for (int j = 0; j < my_n; j += U) {
+  for (int u = 0; u < U; ++u) load(IC<0>{}, u, iter(0, u));
+#pragma unroll
+  for (int u = 0; u < U; ++u) load(IC<1>{}, u, iter(1, u));
+  for (int q = 0; q < rounds; q += 2) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (j + u < my_n) {
-        compute(u);
-        if (j + u + U < my_n) load(u, j + u + U);
-      }
+      compute(IC<0>{}, u);
+      load(IC<0>{}, u, iter(q + 2, u));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      compute(IC<1>{}, u);
+      load(IC<1>{}, u, iter(q + 3, u));
     }
   }
 
   // ---- cross-wave reduction through LDS: wave w's partial tile -> red[w]; then each
-  // thread sums, in wave order, the positions p = tid, tid + THREADS, ...
+  // thread sums, in wave order, the positions p = tid, tid + THREADS, ... below P
   constexpr int P = NB * 64;                     // f32x4 positions per tile
   constexpr int NV = (P + THREADS - 1) / THREADS;
+  static_assert(P <= THREADS || P % THREADS == 0, "whole vectors of positions per thread");
   __shared__ f32x4 red[W][P];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) red[wave][nb * 64 + lane] = acc[nb];
@@ -1421,7 +1449,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
   }
 
   if (sk > 1) {
-    if (!splitk_fixup<f32x4, NV, THREADS>(sum, a, tile, z, sk, gridDim.x)) return;
+    if (!splitk_fixup<f32x4, NV, THREADS, (P < THREADS ? P : THREADS)>(sum, a, tile, z, sk, gridDim.x)) return;
   }
 
   // ---- store: position p = nb*64 + l holds row l%16, columns n0 + 16nb + 4(l/16) + 0..3
@@ -1454,6 +1482,179 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
   else store(std::integral_constant<int, DT_F32>{});
 }
 
+// ================================================================= skinny int4 kernel
+
+// M <= 16, int4 B: the skinny kernel's weight path (codes streamed from HBM into registers,
+// dequantised in registers, 16x16x32 matrix-core steps, waves over interleaved K
+// iterations, cross-wave LDS reduction, split-K fix-up) with the activation rows of the
+// workgroup's K range staged in LDS first. The activations are the one operand every
+// workgroup reads (all of it, or its split's share); as matrix-core fragments straight
+// from memory, each load instruction would touch 16 rows x 4 scattered 16-byte pieces.
+// Here one load instruction moves 1 KiB of one row (buffer_load ... lds), and the fragments
+// are read back from LDS (row pitch K-range x 2 + 16 bytes, so the 16 rows a fragment read
+// touches fall on distinct bank groups).
+// A round covers W * IT iterations of 128 K: its activation slice (16 x W*IT*128 fp16) is
+// loaded straight into LDS, the weight codes and scales of every iteration of the round go
+// to registers, the wave waits for its own direct loads, one barrier, then the iterations
+// are multiplied as their codes arrive. Iterations past the split's end load zeros.
+template <int NB, int W, int IT>
+__global__ __launch_bounds__(W * 64) void gemm_skinny_u4_kernel(KArgs a) {
+  constexpr int THREADS = W * 64;
+  constexpr int KI = 128, H = 4, KL = 32;
+  constexpr int KR = W * IT * KI;             // K per round
+  constexpr int ROW_BYTES = KR * 2;           // one activation row of a round
+  constexpr int PITCH = ROW_BYTES + 16;
+  constexpr int PPR = ROW_BYTES / 1024;       // 1 KiB pieces per row
+  constexpr int NDTL = 16 * PPR;              // direct loads per round
+  static_assert(ROW_BYTES % 1024 == 0 && NDTL % W == 0, "whole 1 KiB pieces, evenly over the waves");
+  constexpr int DPW = NDTL / W;
+  constexpr int P = NB * 64;                  // f32x4 positions of the reduced tile
+  static_assert(P <= THREADS, "one position per thread");
+  constexpr int A_LDS = 16 * PITCH;
+  constexpr int RED_LDS = W * P * 16;
+  constexpr int LDS_BYTES = A_LDS > RED_LDS ? A_LDS : RED_LDS;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, c = lane >> 4;
+  const int tile = blockIdx.x;
+  const int n0 = tile * 16 * NB;
+  const int z = blockIdx.y, sk = gridDim.y;
+  const int kb = z * a.k_chunk;
+  const int ke = min(a.K, kb + a.k_chunk);
+  const int n_it = ke > kb ? (ke - kb) / KI : 0;   // split chunks and K are multiples of 128
+  const int rounds = (n_it + W * IT - 1) / (W * IT);
+
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.B, a.bytesB);
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.S, a.bytesS);
+  const u32x4 wA = rsrc_words(a.A, a.bytesA);
+  const uint32_t lds0 = lds_addr(lds);
+
+  uint32_t offB0[NB], offS0[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = n0 + 16 * nb + r;
+    offB0[nb] = a.b_tiled ? ((uint32_t)((n / 64) * (a.K / 128) + kb / 128) * 64u + (uint32_t)(n % 64)) * 64u + 16u * c
+                          : (uint32_t)n * (uint32_t)(a.K / 2) + (uint32_t)((kb + c * KL) / 2);
+    offS0[nb] = ((uint32_t)((c * KL) >> a.group_log2) * (uint32_t)a.N + (uint32_t)n) * 2u;
+  }
+  const uint32_t b_iter = a.b_tiled ? 4096u : (uint32_t)(KI / 2);
+  // this wave's direct loads: piece j = wave + W*d is row j / PPR, bytes 1024 (j % PPR) of
+  // the row's round slice; lane t takes 16 bytes at 16 t
+  uint32_t dtl_off[DPW], dtl_lds[DPW];
+  int dtl_k[DPW];
+#pragma unroll
+  for (int d = 0; d < DPW; ++d) {
+    const int j = wave + W * d, row = j / PPR, piece = j % PPR;
+    dtl_k[d] = piece * 512 + 8 * lane;                  // K offset in the round
+    dtl_off[d] = row < a.M ? (uint32_t)(row * a.ldA + kb + dtl_k[d]) * 2u : kOOB;
+    dtl_lds[d] = lds0 + (uint32_t)(row * PITCH + piece * 1024);
+  }
+
+  u32x4 bufB[IT][NB];
+  uint16_t bufS[IT][NB];
+  f32x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const _Float16 zb = (_Float16)(-1024 - a.zero), zb16 = (_Float16)(-64 - a.zero);
+  const f16x2 bias = {zb, zb}, bias16 = {zb16, zb16};
+
+  for (int q = 0; q < rounds; ++q) {
+    const int kr = q * KR;   // round start, relative to the split start
+    if (q > 0) __syncthreads();   // every wave is done reading the previous slice
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) {
+      const uint32_t o = kb + kr + dtl_k[d] < ke ? dtl_off[d] + (uint32_t)kr * 2u : kOOB;
+      asm volatile(
+          "s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+          :
+          : "v"(o), "s"(dtl_lds[d]), "s"(wA)
+          : "memory", "m0");
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < IT; ++j) {
+      const int it = q * (W * IT) + wave + W * j;
+      const bool live = it < n_it;
+      const uint32_t sb = live ? (uint32_t)it * b_iter : kOOB;
+      const uint32_t ss = live ? (uint32_t)((kb + it * KI) >> a.group_log2) * (uint32_t)a.N * 2u : kOOB;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        bufB[j][nb] = __builtin_amdgcn_raw_buffer_load_b128(rB, offB0[nb], sb, 0);
+        bufS[j][nb] = __builtin_amdgcn_raw_buffer_load_b16(rS, offS0[nb], ss, 0);
+      }
+    }
+    // this wave's direct loads have landed once at most the IT * 2 * NB register loads
+    // issued after them are outstanding; then the slice is complete for every wave
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int n_after = IT * 2 * NB;
+    static_assert(n_after < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((n_after & 15) | (7 << 4) | (15 << 8) | (((n_after >> 4) & 3) << 14));
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < IT; ++j) {
+      const int itl = wave + W * j;   // iteration within the round
+      const char* arow = lds + r * PITCH + (itl * KI + c * KL) * 2;
+      u32x4 ap[H];
+#pragma unroll
+      for (int h = 0; h < H; ++h)
+        ap[h] = pair_k_and_k4(*reinterpret_cast<const u32x4*>(arow + 16 * h));
+#pragma unroll
+      for (int h = 0; h < H; ++h)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const _Float16 sc = __builtin_bit_cast(_Float16, bufS[j][nb]);
+          const f16x2 s2 = {sc, sc};
+          acc[nb] = mfma16x16x32<F16T>(dequant8_pairs(bufB[j][nb][h], s2, bias, bias16), ap[h], acc[nb]);
+        }
+    }
+  }
+
+  // ---- cross-wave reduction through LDS (the slice's space is reused)
+  __syncthreads();
+  f32x4* red = reinterpret_cast<f32x4*>(lds);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) red[wave * P + nb * 64 + lane] = acc[nb];
+  __syncthreads();
+  f32x4 sum[1];
+  {
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (tid < P) {
+      s = red[tid];
+#pragma unroll
+      for (int w = 1; w < W; ++w) s += red[w * P + tid];
+    }
+    sum[0] = s;
+  }
+  if (sk > 1) {
+    if (!splitk_fixup<f32x4, 1, THREADS, P>(sum, a, tile, z, sk, gridDim.x)) return;
+  }
+  if (tid >= P) return;
+  const int nb = tid / 64, l = tid % 64;
+  const int m = l & 15, n = n0 + 16 * nb + 4 * (l >> 4);
+  if (m >= a.M) return;
+  auto store = [&](auto dt_tag) {
+    constexpr int DT = decltype(dt_tag)::value;
+    using O = typename OutT<DT>::type;
+    O* dst = reinterpret_cast<O*>(a.C) + (size_t)m * a.N + n;
+    if (a.c_vec && n + 4 <= a.N) {
+      typedef O o4 __attribute__((ext_vector_type(4)));
+      o4 w = {cvt_out<DT>(sum[0][0]), cvt_out<DT>(sum[0][1]), cvt_out<DT>(sum[0][2]), cvt_out<DT>(sum[0][3])};
+      *reinterpret_cast<o4*>(dst) = w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < a.N) dst[e] = cvt_out<DT>(sum[0][e]);
+    }
+  };
+  if (a.dtype_c == DT_F16) store(std::integral_constant<int, DT_F16>{});
+  else if (a.dtype_c == DT_BF16) store(std::integral_constant<int, DT_BF16>{});
+  else store(std::integral_constant<int, DT_F32>{});
+}
+
 // ================================================================= instantiation table
 
 using LaunchFn = hipError_t (*)(const Plan&, const KArgs&, hipStream_t);
@@ -1472,6 +1673,13 @@ template <class T, bool U4B, int NB, int W, int U>
 hipError_t launch_skinny(const Plan& p, const KArgs& a, hipStream_t s) {
   dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.grid_z);
   hipLaunchKernelGGL((gemm_skinny_kernel<T, U4B, NB, W, U>), grid, dim3(W * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int NB, int W, int IT>
+hipError_t launch_skinny_u4(const Plan& p, const KArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.grid_z);
+  hipLaunchKernelGGL((gemm_skinny_u4_kernel<NB, W, IT>), grid, dim3(W * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1544,6 +1752,12 @@ struct Variant {
                       16 * (NB), (U4) ? 128 : 64, W, W, 0, 0, U, SLOTS, 0, 0},               \
           &launch_skinny<T, U4, NB, W, U>}
 
+// int4 skinny kernel with the activation slice staged in LDS: (n-blocks, waves, iterations
+// per wave and round, resident workgroups per CU).
+#define SKINNY_U4(NB, W, IT, SLOTS)                                                          \
+  Variant{VariantInfo{KERNEL_SKINNY, DT_F16, DT_U4, 0, 1, 16, 16 * (NB), 128, W, W, 0, 0, IT, \
+                      SLOTS, 0, 0},                                                          \
+          &launch_skinny_u4<NB, W, IT>}
 
 // Instantiation tables, one per translation unit.
 int variants_f16(const Variant** out);

@@ -150,11 +150,24 @@ int gemm_plan(gemm_plan_t* out, int64_t M, int64_t N, int64_t K, int layout_a, i
  * and positive sizes (GEMM_ERR_INVALID_ARG). */
 int gemm_pack_u4_tiled(const void* codes, void* tiled, int64_t N, int64_t K);
 
-/* Bytes of device workspace gemm_run needs for this plan (0 when split_k == 1). */
+/* Bytes of device workspace gemm_run needs for this plan (0 when split_k == 1): 64 KiB of
+ * arrival counters, then one fp32 partial tile per output tile and K split. The workspace
+ * exists because of split-K (BitBLAS PR 268, "SplitK Infer": the K extent is divided among
+ * split_k workgroups per output tile, whose partial sums must then be added): the partials
+ * left after the cross-wave reduction inside each workgroup (IREE PR 19596, the
+ * inter-subgroup reduction description) are added across workgroups through this memory.
+ * Host only. Errors: GEMM_ERR_INVALID_ARG for a NULL plan or NULL `bytes`. */
 int gemm_workspace_size(gemm_plan_t plan, size_t* bytes);
 
 /* Enqueue C = A * B on `stream` (a hipStream_t; NULL is the default stream) and return
- * without synchronising.
+ * without synchronising. The operation is the plain product C(i, j) = sum_k A(i, k) B(k, j)
+ * with fp32 sums and one rounding to dtype_c, for operands whose K index need not be the
+ * contiguous one (Triton PR 5223, "Feature description"). With split_k > 1 the K extent is
+ * divided among split_k workgroups per output tile (BitBLAS PR 268, "SplitK Infer"); inside a
+ * workgroup the waves' partial sums are first reduced through LDS (IREE PR 19596, the
+ * inter-subgroup reduction description), then across the workgroups through `workspace`. For
+ * int4 B the loader dequantises each weight as in gemm_quant_t (BitBLAS PR 268, dequantize
+ * layout example).
  * A, B, C (and scales for int4 B) are device pointers in the plan's layouts, each
  * 16-byte aligned; C must not alias A, B or scales. workspace (16-byte aligned,
  * ws_bytes >= gemm_workspace_size) is needed when split_k > 1, else may be NULL.
@@ -163,17 +176,30 @@ int gemm_workspace_size(gemm_plan_t plan, size_t* bytes);
  * workspace zeroed once can be reused by any plan. Runs that share a workspace must
  * not overlap in time. The rest of the workspace is scratch.
  * Summation order is fixed (split partial sums are added in ascending split index), so
- * repeated runs give identical bits. */
+ * repeated runs give identical bits.
+ * Ownership: every pointer is the caller's; nothing is retained after the call returns.
+ * Errors (returned before anything is enqueued): GEMM_ERR_INVALID_ARG for a NULL plan, A,
+ * B, C, scales (int4) or workspace (split_k > 1); GEMM_ERR_MISALIGNED for a pointer that is
+ * not 16-byte aligned; GEMM_ERR_WORKSPACE_TOO_SMALL; GEMM_ERR_NO_DEVICE when the current
+ * HIP device is not the plan's; GEMM_ERR_HIP when the launch fails. Faults of the kernels
+ * themselves surface at the caller's next synchronisation. */
 int gemm_run(gemm_plan_t plan, const void* A, const void* B, const void* scales, void* C,
              void* workspace, size_t ws_bytes, void* stream);
 
-/* Copy the planner's choices into *info. */
+/* Copy the planner's choices into *info: the macro tile, the LDS padding and row
+ * permutation of the operand tiles (rocm-libraries PR 2487, "Add support for permuting
+ * perpDim" and LdsBlockSizePerPad under "Add support for m0 padding when using LDSTr+DTL"),
+ * and the split-K factor (BitBLAS PR 268, "SplitK Infer"). Host only. Errors:
+ * GEMM_ERR_INVALID_ARG for a NULL plan or NULL `info`. */
 int gemm_plan_query(gemm_plan_t plan, gemm_plan_info_t* info);
 
-/* Free a plan (NULL is ignored). */
+/* Free a host plan made by gemm_plan (NULL is ignored). Bookkeeping of this library, not an
+ * operation of the pages. The plan must not be in use by a gemm_run call still being made
+ * on another host thread; runs already enqueued do not reference it. */
 void gemm_plan_destroy(gemm_plan_t plan);
 
-/* Static text for a status code. */
+/* Static text for a status code (never NULL; unknown codes give "unknown status").
+ * Bookkeeping of this library, not an operation of the pages. */
 const char* gemm_status_string(int status);
 
 /* Row permutation used inside LDS tiles (rocm-libraries PR 2487, "Add support for

@@ -56,6 +56,12 @@ def check_bar(o_bits, inp, rows=None, what=""):
     assert err.max() <= bound, f"{what}: max error {err.max():.3e} > {bound:.3e}"
     rel = np.linalg.norm(g - o64) / np.linalg.norm(o64)
     assert rel <= 2 * u, f"{what}: relative Frobenius error {rel:.3e} > {2 * u:.3e}"
+    # reported beside the bar: the same error against the oracle rounded once to the output
+    # format, the reference the GEMM's tolerance uses
+    r = oracle.decode(oracle.encode(o64, dt), dt)
+    rel_r = np.linalg.norm(g - r) / np.linalg.norm(r)
+    _say(f"  {what}: relative Frobenius error {rel:.3e} against the exact output (bar {2 * u:.3e}), "
+         f"{rel_r:.3e} against the output rounded to {dt}")
     return rel, float(err.max())
 
 

@@ -330,7 +330,8 @@ def test_int4_group_sizes_random_within_tolerance(group, zero):
         check_tolerance(c, ref, "f16", K, amax, bmax, f"int4 g{group} z{zero} M={m}")
 
 
-INT4_SKINNY = ["4x16x2", "4x8x4", "2x8x4", "8x8x2", "2x16x4", "2x16x2", "4x8x2"]
+# 4x4x2 is the int4 default; 4x16x2, 8x16x1, 2x16x2 and 4x8x4 stage the activations in LDS
+INT4_SKINNY = ["4x4x2", "4x16x2", "8x16x1", "2x16x2", "4x8x4", "2x8x4", "2x16x1", "4x8x2", "2x8x2"]
 
 
 @pytest.mark.parametrize("v", INT4_SKINNY)
@@ -352,6 +353,29 @@ def test_int4_skinny_variants_bit_exact(v, sk):
     assert info["kernel"] == 1 and info["split_k"] == sk
     assert (info["tile_n"], info["waves"]) == (16 * int(v.split("x")[0]), int(v.split("x")[1]))
     _, ref = reference(inp, "f16", "f32", int4=True)
+    assert np.array_equal(c, ref)
+
+
+FP16_SKINNY = ["4x4x2", "4x4x1", "4x8x2", "2x8x2"]
+
+
+@pytest.mark.parametrize("v", FP16_SKINNY)
+@pytest.mark.parametrize("M,N,K,sk", [(5, 200, 4104, 1), (16, 520, 8200, 4), (3, 64, 1000, 2)])
+def test_fp16_skinny_variants_bit_exact(v, M, N, K, sk):
+    # integer inputs: every partial sum is exact, so each variant (n-blocks x waves x
+    # iterations per register set) must reproduce the oracle bit for bit, also with K not a
+    # multiple of the wave iteration, ragged rows and columns, and split-K
+    from helpers import env
+    _say("fp16-skinny", v, M, N, K, sk)
+    rng = np.random.default_rng(77)
+    inp = {"M": M, "N": N, "K": K, "layout_a": "row", "layout_b": "col",
+           "A": synth.store(synth.integer_matrix(rng, M, K, -3, 3, "f16"), "row"),
+           "B": synth.store(synth.integer_matrix(rng, K, N, -3, 3, "f16"), "col")}
+    with env(DGEMM_FORCE_SKINNY=v):
+        c, info = run_gpu(inp, "f16", "f32", split_k=sk, guard=8)
+    assert info["kernel"] == 1 and info["split_k"] == sk
+    assert (info["tile_n"], info["waves"]) == (16 * int(v.split("x")[0]), int(v.split("x")[1]))
+    _, ref = reference(inp, "f16", "f32")
     assert np.array_equal(c, ref)
 
 
@@ -413,7 +437,7 @@ def test_transposing_lds_reads_split_k_and_random(la, lb, sched):
     check_tolerance(c, ref, fmt, 328, amax, bmax, "tr")
 
 
-@pytest.mark.parametrize("v,M", [("4x16x2", 5), ("2x8x4", 5), ("8x8x2", 16), ("tile", 384)])
+@pytest.mark.parametrize("v,M", [("4x16x2", 5), ("8x16x1", 16), ("2x8x4", 5), ("2x16x1", 5), ("4x8x2", 16), ("tile", 384)])
 @pytest.mark.parametrize("sk", [1, 4])
 def test_int4_tiled_layout_bit_exact(v, M, sk):
     # the same codes packed by gemm_pack_u4_tiled; the oracle reads the column-major packing.
