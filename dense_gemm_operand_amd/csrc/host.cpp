@@ -130,7 +130,7 @@ int make_plan(Plan& p, int split_k_req) {
       // i.e. ceil(tiles / CUs) * tile area (larger tiles first on ties). A 4-wave tile is
       // charged 5/4 of its area: measured per tile area it runs about that much slower than
       // the 8-wave 256x256 kernels (one wave per SIMD hides less latency).
-      static const int kTiles[][2] = {{256, 256}, {192, 320}, {128, 128}};
+      static const int kTiles[][2] = {{256, 256}, {192, 320}, {128, 128}, {64, 64}};
       // DGEMM_FORCE_TILE=<m>x<n> restricts the choice to one tile (tests, tuning).
       int force_m = 0, force_n = 0;
       if (const char* ft = std::getenv("DGEMM_FORCE_TILE")) std::sscanf(ft, "%dx%d", &force_m, &force_n);
@@ -192,6 +192,8 @@ int make_plan(Plan& p, int split_k_req) {
   // resident per CU (the skinny kernels are small enough for two).
   if (sk == 0) sk = splitk_search(tiles, p.K, k_step, p.cu_count * v.slots_per_cu);
   if (sk > 1 && tiles > kMaxCounters) sk = 1;
+  // schedule 2 (4 waves of 128x128 accumulators) has no split-K fix-up
+  if (v.kernel == KERNEL_TILE && v.sched == 2) sk = 1;
   p.split_k = sk;
   // chunk: ceil(K / sk) rounded up to the per-iteration granule of the kernel
   // int4 splits start on a multiple of 128 K (one skinny-kernel iteration, one block of the
@@ -255,17 +257,17 @@ int gemm_plan(gemm_plan_t* out, int64_t M, int64_t N, int64_t K, int layout_a, i
   } else if (dtype_b != dtype_a) {
     return GEMM_ERR_UNSUPPORTED;
   }
-  // contiguous extents: multiples of 16 bytes (8 16-bit or 16 fp8 elements)
+  // 32-bit buffer offsets: every operand below 2 GiB, every size within int range. Each
+  // extent is bounded first, so that no product below can overflow; the byte limits are
+  // then compared as element counts (lim - 16 and lim divide by eb and ob).
+  const int64_t lim = (int64_t)1 << 31;
   const int64_t eb = dtype_a == DT_F8 ? 1 : 2;
+  const int64_t ob = dtype_c == DT_F32 ? 4 : 2;
+  if (M >= lim || N >= lim || K >= lim) return GEMM_ERR_UNSUPPORTED;
+  // contiguous extents: multiples of 16 bytes (8 16-bit or 16 fp8 elements)
   const int64_t ca = layout_a == 0 ? K : M;
   const int64_t cb = dtype_b == DT_U4 ? K : (layout_b == 0 ? N : K);
   if ((ca * eb) % 16 != 0 || (cb * eb) % 16 != 0) return GEMM_ERR_UNSUPPORTED;
-  // 32-bit buffer offsets: every operand below 2 GiB, every size within int range. Each
-  // extent is bounded first, so that the element counts below cannot overflow; the byte
-  // limits are then compared as element counts (lim - 16 and lim divide by eb and ob).
-  const int64_t lim = (int64_t)1 << 31;
-  const int64_t ob = dtype_c == DT_F32 ? 4 : 2;
-  if (M >= lim || N >= lim || K >= lim) return GEMM_ERR_UNSUPPORTED;
   if (M * K >= (lim - 16) / eb || N * K >= (lim - 16) / eb || M * N >= lim / ob)
     return GEMM_ERR_UNSUPPORTED;
 

@@ -18,8 +18,10 @@ static const Variant kTable[] = {
     TILE_LAYOUTS(BF16T, 256, 256, 2, 2),
     TILE_LAYOUTS(BF16T, 192, 320, 2, 2),
     TILE_LAYOUTS(BF16T, 128, 128, 2, 2),
+    TILE_LAYOUTS(BF16T, 64, 64, 2, 2),
     TILE_LAYOUTS_DTL(BF16T, 256, 256, 2, 2),
     TILE_LAYOUTS_DTLTR(BF16T, 256, 256, 2, 4),
+    TILE_LAYOUTS_W4(BF16T),
 };
 
 int variants_bf16(const Variant** out) {

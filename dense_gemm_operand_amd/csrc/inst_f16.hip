@@ -18,8 +18,10 @@ static const Variant kTable[] = {
     TILE_LAYOUTS(F16T, 256, 256, 2, 2),
     TILE_LAYOUTS(F16T, 192, 320, 2, 2),
     TILE_LAYOUTS(F16T, 128, 128, 2, 2),
+    TILE_LAYOUTS(F16T, 64, 64, 2, 2),
     TILE_LAYOUTS_DTL(F16T, 256, 256, 2, 2),
     TILE_LAYOUTS_DTLTR(F16T, 256, 256, 2, 4),
+    TILE_LAYOUTS_W4(F16T),
 };
 
 int variants_f16(const Variant** out) {

@@ -13,18 +13,13 @@ static const Variant kTable[] = {
     // (DGEMM_FORCE_SKINNY).
     SKINNY(F16T, false, 4, 4, 2, 2),
     SKINNY(BF16T, false, 4, 4, 2, 2),
+    SKINNY(F16T, true, 2, 8, 2, 1),
     SKINNY(F16T, true, 4, 4, 2, 1),
-    SKINNY_U4(4, 16, 2, 1),
-    SKINNY_U4(8, 16, 1, 1),
-    SKINNY_U4(2, 16, 2, 1),
-    SKINNY_U4(4, 8, 4, 1),
     SKINNY(F16T, true, 2, 8, 4, 1),
     SKINNY(F16T, false, 4, 4, 1, 2),
     SKINNY(F16T, false, 4, 8, 2, 1),
     SKINNY(F16T, false, 2, 8, 2, 1),
-    SKINNY(F16T, true, 2, 16, 1, 1),
     SKINNY(F16T, true, 4, 8, 2, 1),
-    SKINNY(F16T, true, 2, 8, 2, 1),
     // int4 B (column-major codes), A either layout; row-major A: the ping-pong schedule with
     // A loaded straight into LDS (column-major A: the pipeline, which measured faster)
     TILE_X(F16T, true, true, true, 256, 256, 2, 4, true, true, 1),

@@ -59,6 +59,24 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // Buffer offset beyond every operand's num_records: such a load returns zeros.
 constexpr uint32_t kOOB = 0x80000000u;
 
+// Over-synchronised build (compiled with -DDGEMM_OVERSYNC=1 into a separate test library):
+// in the tiled kernel's main loops every phase ends with a wait for every outstanding load
+// and LDS access and a workgroup barrier. It computes the same sums in the same order, so
+// its results must equal the normal build's bit for bit; a difference would expose an LDS
+// race that the hand-ordered waits and barriers of the normal build leave open.
+#ifndef DGEMM_OVERSYNC
+#define DGEMM_OVERSYNC 0
+#endif
+constexpr bool kOverSync = DGEMM_OVERSYNC != 0;
+__device__ __forceinline__ void oversync_point() {
+  if constexpr (kOverSync) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 struct F16T {};
 struct BF16T {};
 struct F8T {};   // OCP 8-bit E4M3 (bias 7, no infinities, S.1111.111 is NaN)
@@ -447,15 +465,18 @@ struct DtlOperand {
   __device__ __forceinline__ void issue(const u32x4& rs, uint32_t base, int wave, uint32_t d,
                                         int lim) const {
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const uint32_t o = kofs[j] < lim ? off[j] + d : kOOB;
-      const uint32_t m0v = base + (uint32_t)(wave * NI + j) * 1024u;
-      asm volatile(
-          "s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-          :
-          : "v"(o), "s"(m0v), "s"(rs)
-          : "memory", "m0");
-    }
+    for (int j = 0; j < NI; ++j) issue_one(rs, base, wave, d, lim, j);
+  }
+  // Load instruction j of the step only.
+  __device__ __forceinline__ void issue_one(const u32x4& rs, uint32_t base, int wave, uint32_t d,
+                                            int lim, int j) const {
+    const uint32_t o = kofs[j] < lim ? off[j] + d : kOOB;
+    const uint32_t m0v = base + (uint32_t)(wave * NI + j) * 1024u;
+    asm volatile(
+        "s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+        :
+        : "v"(o), "s"(m0v), "s"(rs)
+        : "memory", "m0");
   }
 };
 
@@ -501,15 +522,17 @@ struct DtlTrOperand {
   __device__ __forceinline__ void issue(const u32x4& rs, uint32_t base, int wave, uint32_t d,
                                         int lim) const {
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const uint32_t o = krow[j] < lim ? off[j] + d : kOOB;
-      const uint32_t m0v = base + (uint32_t)(wave * NI + j) * BLOCK_BYTES;
-      asm volatile(
-          "s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-          :
-          : "v"(o), "s"(m0v), "s"(rs)
-          : "memory", "m0");
-    }
+    for (int j = 0; j < NI; ++j) issue_one(rs, base, wave, d, lim, j);
+  }
+  __device__ __forceinline__ void issue_one(const u32x4& rs, uint32_t base, int wave, uint32_t d,
+                                            int lim, int j) const {
+    const uint32_t o = krow[j] < lim ? off[j] + d : kOOB;
+    const uint32_t m0v = base + (uint32_t)(wave * NI + j) * BLOCK_BYTES;
+    asm volatile(
+        "s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+        :
+        : "v"(o), "s"(m0v), "s"(rs)
+        : "memory", "m0");
   }
   // Lane's byte offset (stage-relative) for sub-step 0, read 0, fragment block 0, of the
   // wave's rows starting at wrow; sub-step kk adds 8 * BLOCK_BYTES * kk, read 1 adds 512,
@@ -576,6 +599,8 @@ struct TileCfg {
   static constexpr int B16 = B_TR ? TB::BYTES / 16 : MT_N * PB16;
   static constexpr int STAGE16 = A16 + B16;
   static constexpr int LDS_BYTES = 2 * STAGE16 * 16;
+  // LDS the kernel allocates (every schedule: the two stages)
+  static constexpr int lds_alloc(int) { return LDS_BYTES; }
   // Register sets for in-flight global data: two (loads two steps ahead) unless a thread
   // owns more than four blocks, where the second set would not fit in the register file.
   static constexpr int NSETS = (SA + SB) > 4 ? 1 : 2;
@@ -636,7 +661,7 @@ constexpr bool epilogue_runs16_ok() {
 }
 
 template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN,
-          int LROWS, bool PP, int DTL>
+          int LROWS, int SCHED, int DTL>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   using Cfg = TileCfg<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, LROWS, DTL>;
   using OpA = typename Cfg::OpA;
@@ -648,7 +673,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   constexpr int SA1 = SA > 0 ? SA : 1, SB1 = SB > 0 ? SB : 1;  // array extents
   constexpr int EB = Cfg::EB;
   constexpr RowPerm PA = Cfg::PA, PB = Cfg::PB;
-  __shared__ __attribute__((aligned(16))) u32x4 lds[Cfg::LDS_BYTES / 16];
+  constexpr int LDS_ALLOC = Cfg::lds_alloc(SCHED);
+  __shared__ __attribute__((aligned(16))) u32x4 lds[LDS_ALLOC / 16];
   char* const ldsb = reinterpret_cast<char*>(lds);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -899,11 +925,15 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     }
     sub(IC<0>{});
     __builtin_amdgcn_sched_barrier(0);
+    oversync_point();
     sub(IC<1>{});
     __builtin_amdgcn_sched_barrier(0);
+    oversync_point();
     sub(IC<2>{});
     __builtin_amdgcn_sched_barrier(0);
+    oversync_point();
     sub(IC<3>{});
+    oversync_point();
     if constexpr (Cfg::ANY_DTL) __builtin_amdgcn_s_waitcnt(0);  // every load of the step
     __syncthreads();
   };
@@ -982,6 +1012,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     read_b(1, IC<1>{});
     slots(IC<0>{});
     __builtin_amdgcn_sched_barrier(0);
+    oversync_point();
     // half 1
     if constexpr (LOAD) load_part(CUR_, s + 2, IC<2>{}, IC<4>{});
     if constexpr (STORE) {
@@ -1002,7 +1033,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   };
 
   using TRUE = std::integral_constant<bool, true>;
-  if constexpr (!PP) {
+  if constexpr (SCHED == 0) {
     // Every step loads two ahead and stores one ahead; loads past the split's end use
     // out-of-range offsets and return zeros, so the loop runs an even number of steps (a
     // padding step multiplies zeros and leaves the sums exact) and has no drain code.
@@ -1023,6 +1054,101 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
       run_step(s, IC<0>{}, LOADS{}, TRUE{});
       run_step(s + 1, IC<1>{}, LOADS{}, TRUE{});
     }
+  } else if constexpr (SCHED == 2) {
+    // One wave per SIMD (4 waves of 128x128), every operand straight into LDS, one barrier
+    // per step, placed after sub-step 2. Per step s (LDS buffer CUR = s % 2):
+    //   sub-step 0: 16 multiplies on fragment set 0; read sub-step 1's fragments (set 1)
+    //   sub-step 1: 16 multiplies on set 1; read sub-step 2's fragments (set 0)
+    //   sub-step 2: 16 multiplies on set 0; read sub-step 3's fragments (set 1)
+    //   wait for this wave's direct loads (step s+1, issued a step ago) and its reads; barrier
+    //   sub-step 3: 16 multiplies on set 1; read step s+1's sub-step 0 fragments from the
+    //               other buffer (set 0); issue step s+2's direct loads into buffer CUR
+    // After the barrier of step s every wave has finished reading buffer CUR (its last
+    // reads completed before the barrier) and every wave's loads of step s+1 have landed,
+    // so sub-step 3 can both read step s+1 and refill buffer CUR with step s+2. The
+    // matrix cores never wait for a read issued after a barrier: the 16 multiplies of
+    // sub-step 3 use fragments read before it.
+    static_assert(SA == 0 && SB == 0 && !Cfg::F8 && NS == 2, "every operand direct-to-LDS, 16-bit");
+    constexpr int NIA = Cfg::A_DTL ? Cfg::DA::NI : (Cfg::A_TR ? Cfg::TA::NI : 0);
+    constexpr int NIB = Cfg::B_DTL ? Cfg::DB::NI : (Cfg::B_TR ? Cfg::TB::NI : 0);
+    constexpr int NLD = NIA + NIB;   // direct loads per wave and step
+    static_assert(NLD == TM * TN, "one direct load per multiply of sub-step 3");
+    u32x4 fa[2][TM], fb[2][TN];
+    auto read_frag = [&](int buf, int kk, int q, int f) {
+      // fragment f of sub-step kk: A blocks 0..TM-1, then B blocks 0..TN-1
+      const u32x4* st = lds + buf * Cfg::STAGE16;
+      const char* sbytes = reinterpret_cast<const char*>(st);
+      if (f < TM) {
+        const int i = f;
+        if constexpr (Cfg::A_TR)
+          fa[q][i] = tr_fragment(sbytes + a_tr + 8 * Cfg::TA::BLOCK_BYTES * kk + 64 * i);
+        else
+          fa[q][i] = st[a_rd[kk] + i * 32 * PA16];
+      } else {
+        const int j = f - TM;
+        if constexpr (Cfg::B_TR)
+          fb[q][j] = tr_fragment(sbytes + b_tr + 8 * Cfg::TB::BLOCK_BYTES * kk + 64 * j);
+        else
+          fb[q][j] = st[b_rd[kk] + j * 32 * PB16];
+      }
+    };
+    auto dtl_one = [&](int step, int buf, int g) {
+      const uint32_t sA = lds0 + buf * Cfg::STAGE16 * 16;
+      const int lim = klen - step * BK;
+      if (g < NIA) {
+        if constexpr (Cfg::A_DTL) da.issue_one(wA, sA, wave, dA * (uint32_t)step, lim, g);
+        if constexpr (Cfg::A_TR) ta.issue_one(wA, sA, wave, dA * (uint32_t)step, lim, g);
+      } else {
+        if constexpr (Cfg::B_DTL) db.issue_one(wB, sA + Cfg::A16 * 16, wave, dB * (uint32_t)step, lim, g - NIA);
+        if constexpr (Cfg::B_TR) tb.issue_one(wB, sA + Cfg::A16 * 16, wave, dB * (uint32_t)step, lim, g - NIA);
+      }
+    };
+    // Sub-step kk of a step in buffer CUR: multiply set Q, and after the multiply g, read
+    // fragment g of the next sub-step (from buffer RBUF, sub-step RKK, into set Q ^ 1) and,
+    // in sub-step 3, issue direct load g of step s + 2 into buffer CUR.
+    auto substep = [&](int s, auto CUR_, auto KK_) {
+      constexpr int CUR = decltype(CUR_)::value, kk = decltype(KK_)::value;
+      constexpr int Q = kk & 1;
+      constexpr int RBUF = kk < 3 ? CUR : CUR ^ 1, RKK = (kk + 1) & 3;
+#pragma unroll
+      for (int g = 0; g < TM * TN; ++g) {
+        const int i = g / TN, j = g % TN;
+        acc[i * TN + j] = mfma32x32x16<T>(fb[Q][j], fa[Q][i], acc[i * TN + j]);
+        if (g < TM + TN) read_frag(RBUF, RKK, Q ^ 1, g);
+        if constexpr (kk == 3) dtl_one(s + 2, CUR, g);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    auto step_w4 = [&](int s, auto CUR_) {
+      substep(s, CUR_, IC<0>{});
+      substep(s, CUR_, IC<1>{});
+      substep(s, CUR_, IC<2>{});
+      oversync_point();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of step s+1 and its reads of step s
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      substep(s, CUR_, IC<3>{});
+      oversync_point();
+    };
+    dtl(0, IC<0>{});
+    dtl(1, IC<1>{});
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((NLD & 15) | (7 << 4) | (15 << 8) | (((NLD >> 4) & 3) << 14));  // step 0 landed
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = 0; f < TM + TN; ++f) read_frag(0, 0, 0, f);
+    for (int s = 0; s < nt; s += 2) {
+      // two steps per iteration so the buffer indices are compile-time; an odd step count
+      // ends with a step of zeros (its loads lie past the split)
+      step_w4(s, IC<0>{});
+      step_w4(s + 1, IC<1>{});
+    }
+    // the last direct loads (zeros past the split) still write LDS, which the epilogue
+    // reuses: every wave waits for its own, then one more barrier for all
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   } else {
     // Ping-pong schedule. The waves form two groups (wave rows wm = 0 and 1, one wave of
     // each on every SIMD) that run the same program one phase apart, so in every phase
@@ -1094,6 +1220,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     // otherwise drift across a plain barrier).
     auto phase_barrier = [&]() {
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kOverSync) __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -1178,8 +1305,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     }
   }
 
-  if (sk > 1) {
-    if (!splitk_fixup<f32x16, TM * TN, THREADS>(acc, a, tile, z, sk, tiles)) return;
+  // (schedule 2 is planned without split-K: its 256 accumulators leave no registers for
+  // the fix-up's element-wise sums)
+  if constexpr (SCHED != 2) {
+    if (sk > 1) {
+      if (!splitk_fixup<f32x16, TM * TN, THREADS>(acc, a, tile, z, sk, tiles)) return;
+    }
   }
 
   // ---- epilogue: block (i, j), lane l holds logical row fwd_A(LDS row 32i + l%32) and,
@@ -1194,7 +1325,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     constexpr int OB = OutT<DT>::bytes;
     constexpr int ROW_BYTES = MT_N * OB;
     constexpr int CP = ROW_BYTES + 16;                    // LDS pitch of the C tile
-    constexpr int RPP0 = Cfg::LDS_BYTES / CP;
+    constexpr int RPP0 = LDS_ALLOC / CP;
     constexpr int RPP = RPP0 >= MT_M ? MT_M : (RPP0 / 32) * 32;  // rows per pass
     constexpr int NPASS = (MT_M + RPP - 1) / RPP;
     constexpr int CPR = ROW_BYTES / 16;                   // 16-byte chunks per row
@@ -1273,6 +1404,47 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
       __syncthreads();
     }
   };
+  // Schedule 2 (one wave of 128x128 per SIMD) stores C straight from the accumulators: lane
+  // l of block (i, j) holds row 32i + l%32 and, for g = 0..3, the four consecutive columns
+  // 32j + 8g + 4(l/32) + 0..3, so each store is one 4-element vector; the lanes of a store
+  // cover 16 contiguous bytes of 32 rows (fp16), and the 16 stores of a block fill whole
+  // 128-byte lines of those rows. No LDS round trip, and no accumulator needs to wait for a
+  // second pass (the two-pass LDS epilogue of an fp32 tile would not fit the registers).
+  auto epilogue_direct = [&](auto dt_tag) {
+    constexpr int DT = decltype(dt_tag)::value;
+    using O = typename OutT<DT>::type;
+    typedef O o4 __attribute__((ext_vector_type(4)));
+    O* Cg = reinterpret_cast<O*>(a.C);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int gm = m0 + wm * Cfg::WT_M + i * 32 + r32;
+      if (gm >= a.M) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int gn = n0 + wn * Cfg::WT_N + j * 32 + 8 * g + 4 * kh;
+          const f32x16& v = acc[i * TN + j];
+          O* dst = Cg + (size_t)gm * a.N + gn;
+          if (a.c_vec && gn + 4 <= a.N) {
+            o4 w = {cvt_out<DT>(v[4 * g]), cvt_out<DT>(v[4 * g + 1]), cvt_out<DT>(v[4 * g + 2]),
+                    cvt_out<DT>(v[4 * g + 3])};
+            *reinterpret_cast<o4*>(dst) = w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (gn + e < a.N) dst[e] = cvt_out<DT>(v[4 * g + e]);
+          }
+        }
+      }
+    }
+  };
+  if constexpr (SCHED == 2) {
+    if (a.dtype_c == DT_F16) epilogue_direct(std::integral_constant<int, DT_F16>{});
+    else if (a.dtype_c == DT_BF16) epilogue_direct(std::integral_constant<int, DT_BF16>{});
+    else epilogue_direct(std::integral_constant<int, DT_F32>{});
+    return;
+  }
   // The C tile reuses the operand LDS: every wave is past the loop's last barrier.
   if (a.dtype_c == DT_F16) epilogue(std::integral_constant<int, DT_F16>{});
   else if (a.dtype_c == DT_BF16) epilogue(std::integral_constant<int, DT_BF16>{});
@@ -1326,7 +1498,10 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
   // so the sum stays below 2^32 and lies past every buffer's end.
   uint32_t offA0 = 0, offB0[NB], offS0[NB];
   if constexpr (U4B) {
-    offA0 = (uint32_t)(r * a.ldA + kb + c * KL) * 2u;
+    // activations, coalesced: load h of an iteration takes rows 4h + lane/16, the 16-byte
+    // chunk lane%16 of each row's 256 bytes (whole 128-byte lines, 1 KiB per load); the
+    // fragments are then formed through the wave's LDS slot (transpose_a below)
+    offA0 = (uint32_t)((lane >> 4) * a.ldA + kb + 8 * (lane & 15)) * 2u;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int n = n0 + 16 * nb + r;
@@ -1350,7 +1525,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
       const uint32_t ss = live ? (uint32_t)((kb + it * KI) >> a.group_log2) * (uint32_t)a.N * 2u : kOOB;
 #pragma unroll
       for (int h = 0; h < H; ++h)
-        bufA[SET][u][h] = __builtin_amdgcn_raw_buffer_load_b128(rA, offA0 + 16u * h, sa, 0);
+        bufA[SET][u][h] = __builtin_amdgcn_raw_buffer_load_b128(rA, offA0 + (uint32_t)(4 * h * a.ldA) * 2u, sa, 0);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         bufB[SET][u][nb][0] = __builtin_amdgcn_raw_buffer_load_b128(rB, offB0[nb], sb, 0);
@@ -1381,6 +1556,23 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
 
   const _Float16 zb = (_Float16)(-1024 - a.zero), zb16 = (_Float16)(-64 - a.zero);
   const f16x2 bias = {zb, zb}, bias16 = {zb16, zb16};
+  // int4: the wave's LDS slot turns one iteration's coalesced activation loads (load h: rows
+  // 4h + c', chunk r') into matrix-core fragments (fragment h: row r, chunk 4c + h, i.e. K
+  // indices 32c + 8h .. +7, the K indices of the codes in dword h of the lane's 16 bytes).
+  // The row pitch of 272 bytes puts the 16 rows a fragment read touches on 16 distinct
+  // 16-byte bank groups. Only the wave itself uses its slot, and one wave's LDS accesses
+  // complete in order, so no barrier is needed.
+  constexpr int APITCH = 272;
+  __shared__ __attribute__((aligned(16))) char aslot[U4B ? W : 1][U4B ? 16 * APITCH : 16];
+  auto transpose_a = [&](const u32x4 (&v)[H], int h) {
+    char* slot = aslot[U4B ? wave : 0];
+    if (h == 0) {
+#pragma unroll
+      for (int g = 0; g < H; ++g)
+        *reinterpret_cast<u32x4*>(slot + (4 * g + (lane >> 4)) * APITCH + 16 * (lane & 15)) = v[g];
+    }
+    return *reinterpret_cast<const u32x4*>(slot + r * APITCH + (4 * c + h) * 16);
+  };
   auto compute = [&](auto SET_, int u) {
     constexpr int SET = decltype(SET_)::value;
     if constexpr (U4B) {
@@ -1388,7 +1580,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
       // iteration for all NB blocks
       u32x4 ap[H];
 #pragma unroll
-      for (int h = 0; h < H; ++h) ap[h] = pair_k_and_k4(bufA[SET][u][h]);
+      for (int h = 0; h < H; ++h) ap[h] = pair_k_and_k4(transpose_a(bufA[SET][u], h));
 #pragma unroll
       for (int h = 0; h < H; ++h)
 #pragma unroll
@@ -1482,185 +1674,12 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
   else store(std::integral_constant<int, DT_F32>{});
 }
 
-// ================================================================= skinny int4 kernel
-
-// M <= 16, int4 B: the skinny kernel's weight path (codes streamed from HBM into registers,
-// dequantised in registers, 16x16x32 matrix-core steps, waves over interleaved K
-// iterations, cross-wave LDS reduction, split-K fix-up) with the activation rows of the
-// workgroup's K range staged in LDS first. The activations are the one operand every
-// workgroup reads (all of it, or its split's share); as matrix-core fragments straight
-// from memory, each load instruction would touch 16 rows x 4 scattered 16-byte pieces.
-// Here one load instruction moves 1 KiB of one row (buffer_load ... lds), and the fragments
-// are read back from LDS (row pitch K-range x 2 + 16 bytes, so the 16 rows a fragment read
-// touches fall on distinct bank groups).
-// A round covers W * IT iterations of 128 K: its activation slice (16 x W*IT*128 fp16) is
-// loaded straight into LDS, the weight codes and scales of every iteration of the round go
-// to registers, the wave waits for its own direct loads, one barrier, then the iterations
-// are multiplied as their codes arrive. Iterations past the split's end load zeros.
-template <int NB, int W, int IT>
-__global__ __launch_bounds__(W * 64) void gemm_skinny_u4_kernel(KArgs a) {
-  constexpr int THREADS = W * 64;
-  constexpr int KI = 128, H = 4, KL = 32;
-  constexpr int KR = W * IT * KI;             // K per round
-  constexpr int ROW_BYTES = KR * 2;           // one activation row of a round
-  constexpr int PITCH = ROW_BYTES + 16;
-  constexpr int PPR = ROW_BYTES / 1024;       // 1 KiB pieces per row
-  constexpr int NDTL = 16 * PPR;              // direct loads per round
-  static_assert(ROW_BYTES % 1024 == 0 && NDTL % W == 0, "whole 1 KiB pieces, evenly over the waves");
-  constexpr int DPW = NDTL / W;
-  constexpr int P = NB * 64;                  // f32x4 positions of the reduced tile
-  static_assert(P <= THREADS, "one position per thread");
-  constexpr int A_LDS = 16 * PITCH;
-  constexpr int RED_LDS = W * P * 16;
-  constexpr int LDS_BYTES = A_LDS > RED_LDS ? A_LDS : RED_LDS;
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r = lane & 15, c = lane >> 4;
-  const int tile = blockIdx.x;
-  const int n0 = tile * 16 * NB;
-  const int z = blockIdx.y, sk = gridDim.y;
-  const int kb = z * a.k_chunk;
-  const int ke = min(a.K, kb + a.k_chunk);
-  const int n_it = ke > kb ? (ke - kb) / KI : 0;   // split chunks and K are multiples of 128
-  const int rounds = (n_it + W * IT - 1) / (W * IT);
-
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.B, a.bytesB);
-  const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.S, a.bytesS);
-  const u32x4 wA = rsrc_words(a.A, a.bytesA);
-  const uint32_t lds0 = lds_addr(lds);
-
-  uint32_t offB0[NB], offS0[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int n = n0 + 16 * nb + r;
-    offB0[nb] = a.b_tiled ? ((uint32_t)((n / 64) * (a.K / 128) + kb / 128) * 64u + (uint32_t)(n % 64)) * 64u + 16u * c
-                          : (uint32_t)n * (uint32_t)(a.K / 2) + (uint32_t)((kb + c * KL) / 2);
-    offS0[nb] = ((uint32_t)((c * KL) >> a.group_log2) * (uint32_t)a.N + (uint32_t)n) * 2u;
-  }
-  const uint32_t b_iter = a.b_tiled ? 4096u : (uint32_t)(KI / 2);
-  // this wave's direct loads: piece j = wave + W*d is row j / PPR, bytes 1024 (j % PPR) of
-  // the row's round slice; lane t takes 16 bytes at 16 t
-  uint32_t dtl_off[DPW], dtl_lds[DPW];
-  int dtl_k[DPW];
-#pragma unroll
-  for (int d = 0; d < DPW; ++d) {
-    const int j = wave + W * d, row = j / PPR, piece = j % PPR;
-    dtl_k[d] = piece * 512 + 8 * lane;                  // K offset in the round
-    dtl_off[d] = row < a.M ? (uint32_t)(row * a.ldA + kb + dtl_k[d]) * 2u : kOOB;
-    dtl_lds[d] = lds0 + (uint32_t)(row * PITCH + piece * 1024);
-  }
-
-  u32x4 bufB[IT][NB];
-  uint16_t bufS[IT][NB];
-  f32x4 acc[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const _Float16 zb = (_Float16)(-1024 - a.zero), zb16 = (_Float16)(-64 - a.zero);
-  const f16x2 bias = {zb, zb}, bias16 = {zb16, zb16};
-
-  for (int q = 0; q < rounds; ++q) {
-    const int kr = q * KR;   // round start, relative to the split start
-    if (q > 0) __syncthreads();   // every wave is done reading the previous slice
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int d = 0; d < DPW; ++d) {
-      const uint32_t o = kb + kr + dtl_k[d] < ke ? dtl_off[d] + (uint32_t)kr * 2u : kOOB;
-      asm volatile(
-          "s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
-          :
-          : "v"(o), "s"(dtl_lds[d]), "s"(wA)
-          : "memory", "m0");
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < IT; ++j) {
-      const int it = q * (W * IT) + wave + W * j;
-      const bool live = it < n_it;
-      const uint32_t sb = live ? (uint32_t)it * b_iter : kOOB;
-      const uint32_t ss = live ? (uint32_t)((kb + it * KI) >> a.group_log2) * (uint32_t)a.N * 2u : kOOB;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        bufB[j][nb] = __builtin_amdgcn_raw_buffer_load_b128(rB, offB0[nb], sb, 0);
-        bufS[j][nb] = __builtin_amdgcn_raw_buffer_load_b16(rS, offS0[nb], ss, 0);
-      }
-    }
-    // this wave's direct loads have landed once at most the IT * 2 * NB register loads
-    // issued after them are outstanding; then the slice is complete for every wave
-    __builtin_amdgcn_sched_barrier(0);
-    constexpr int n_after = IT * 2 * NB;
-    static_assert(n_after < 64, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt((n_after & 15) | (7 << 4) | (15 << 8) | (((n_after >> 4) & 3) << 14));
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < IT; ++j) {
-      const int itl = wave + W * j;   // iteration within the round
-      const char* arow = lds + r * PITCH + (itl * KI + c * KL) * 2;
-      u32x4 ap[H];
-#pragma unroll
-      for (int h = 0; h < H; ++h)
-        ap[h] = pair_k_and_k4(*reinterpret_cast<const u32x4*>(arow + 16 * h));
-#pragma unroll
-      for (int h = 0; h < H; ++h)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const _Float16 sc = __builtin_bit_cast(_Float16, bufS[j][nb]);
-          const f16x2 s2 = {sc, sc};
-          acc[nb] = mfma16x16x32<F16T>(dequant8_pairs(bufB[j][nb][h], s2, bias, bias16), ap[h], acc[nb]);
-        }
-    }
-  }
-
-  // ---- cross-wave reduction through LDS (the slice's space is reused)
-  __syncthreads();
-  f32x4* red = reinterpret_cast<f32x4*>(lds);
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) red[wave * P + nb * 64 + lane] = acc[nb];
-  __syncthreads();
-  f32x4 sum[1];
-  {
-    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (tid < P) {
-      s = red[tid];
-#pragma unroll
-      for (int w = 1; w < W; ++w) s += red[w * P + tid];
-    }
-    sum[0] = s;
-  }
-  if (sk > 1) {
-    if (!splitk_fixup<f32x4, 1, THREADS, P>(sum, a, tile, z, sk, gridDim.x)) return;
-  }
-  if (tid >= P) return;
-  const int nb = tid / 64, l = tid % 64;
-  const int m = l & 15, n = n0 + 16 * nb + 4 * (l >> 4);
-  if (m >= a.M) return;
-  auto store = [&](auto dt_tag) {
-    constexpr int DT = decltype(dt_tag)::value;
-    using O = typename OutT<DT>::type;
-    O* dst = reinterpret_cast<O*>(a.C) + (size_t)m * a.N + n;
-    if (a.c_vec && n + 4 <= a.N) {
-      typedef O o4 __attribute__((ext_vector_type(4)));
-      o4 w = {cvt_out<DT>(sum[0][0]), cvt_out<DT>(sum[0][1]), cvt_out<DT>(sum[0][2]), cvt_out<DT>(sum[0][3])};
-      *reinterpret_cast<o4*>(dst) = w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (n + e < a.N) dst[e] = cvt_out<DT>(sum[0][e]);
-    }
-  };
-  if (a.dtype_c == DT_F16) store(std::integral_constant<int, DT_F16>{});
-  else if (a.dtype_c == DT_BF16) store(std::integral_constant<int, DT_BF16>{});
-  else store(std::integral_constant<int, DT_F32>{});
-}
-
 // ================================================================= instantiation table
 
 using LaunchFn = hipError_t (*)(const Plan&, const KArgs&, hipStream_t);
 
 template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN, int LROWS,
-          bool PP, int DTL>
+          int PP, int DTL>
 hipError_t launch_tile(const Plan& p, const KArgs& a, hipStream_t s) {
   using Cfg = TileCfg<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, LROWS, DTL>;
   dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.grid_z);
@@ -1673,13 +1692,6 @@ template <class T, bool U4B, int NB, int W, int U>
 hipError_t launch_skinny(const Plan& p, const KArgs& a, hipStream_t s) {
   dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.grid_z);
   hipLaunchKernelGGL((gemm_skinny_kernel<T, U4B, NB, W, U>), grid, dim3(W * 64), 0, s, a);
-  return hipGetLastError();
-}
-
-template <int NB, int W, int IT>
-hipError_t launch_skinny_u4(const Plan& p, const KArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.grid_z);
-  hipLaunchKernelGGL((gemm_skinny_u4_kernel<NB, W, IT>), grid, dim3(W * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1696,7 +1708,7 @@ struct Variant {
   Variant{VariantInfo{KERNEL_TILE, dt_code<T>(), (U4) ? DT_U4 : dt_code<T>(), (AKC) ? 0 : 1,  \
                       (BKC) ? 1 : 0, MTM, MTN,                                               \
                       TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::BK, (WM) * (WN), 1, PERM, \
-                      TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::LDS_BYTES,      \
+                      TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::lds_alloc(PP),  \
                       TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::NSETS, 1, PP,   \
                       (TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::A_DTL ? 1 : 0) | \
                       (TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::B_DTL ? 2 : 0) | \
@@ -1741,6 +1753,14 @@ struct Variant {
   TILE_X(T, false, true, false, MTM, MTN, WM, WN, true, true, 2),                          \
   TILE_X(T, false, false, false, MTM, MTN, WM, WN, true, true, 2)
 
+// Every layout on schedule 2 (4 waves of 128x128, every operand straight into LDS, the
+// transposed ones transposed by the LDS reads, one barrier per step after sub-step 2).
+#define TILE_LAYOUTS_W4(T)                                                                   \
+  TILE_X(T, true, true, false, 256, 256, 2, 2, true, 2, 1),                                \
+  TILE_X(T, false, true, false, 256, 256, 2, 2, true, 2, 2),                               \
+  TILE_X(T, true, false, false, 256, 256, 2, 2, true, 2, 2),                               \
+  TILE_X(T, false, false, false, 256, 256, 2, 2, true, 2, 2)
+
 #define TILE_LAYOUTS_PP(T, MTM, MTN, WM, WN)                                                 \
   TILE_PP(T, true, true, false, MTM, MTN, WM, WN, true, true),                             \
   TILE_PP(T, true, false, false, MTM, MTN, WM, WN, true, true),                            \
@@ -1752,12 +1772,6 @@ struct Variant {
                       16 * (NB), (U4) ? 128 : 64, W, W, 0, 0, U, SLOTS, 0, 0},               \
           &launch_skinny<T, U4, NB, W, U>}
 
-// int4 skinny kernel with the activation slice staged in LDS: (n-blocks, waves, iterations
-// per wave and round, resident workgroups per CU).
-#define SKINNY_U4(NB, W, IT, SLOTS)                                                          \
-  Variant{VariantInfo{KERNEL_SKINNY, DT_F16, DT_U4, 0, 1, 16, 16 * (NB), 128, W, W, 0, 0, IT, \
-                      SLOTS, 0, 0},                                                          \
-          &launch_skinny_u4<NB, W, IT>}
 
 // Instantiation tables, one per translation unit.
 int variants_f16(const Variant** out);
