@@ -25,6 +25,9 @@ GEMM_ERR_WORKSPACE_TOO_SMALL = -4
 GEMM_ERR_NO_DEVICE = -5
 GEMM_ERR_HIP = -6
 
+# Per-GPU workspace of gemm_run_noalloc (include/dgemm.h GEMM_NOALLOC_WORKSPACE_BYTES).
+NOALLOC_WORKSPACE_BYTES = 32 << 20
+
 LAYOUT = {"row": GEMM_ROW_MAJOR, "col": GEMM_COL_MAJOR, "u4_tiled": GEMM_U4_TILED}
 DTYPE = {"f32": GEMM_F32, "f16": GEMM_F16, "bf16": GEMM_BF16, "u4": GEMM_U4, "f8": GEMM_F8}
 
@@ -80,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_workspace_size.restype = i32
         L.gemm_run.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.gemm_run.restype = i32
+        L.gemm_run_noalloc.argtypes = [vp, vp, vp, vp, vp, vp]
+        L.gemm_run_noalloc.restype = i32
         L.gemm_plan_query.argtypes = [vp, ctypes.POINTER(gemm_plan_info_t)]
         L.gemm_plan_query.restype = i32
         L.gemm_plan_destroy.argtypes = [vp]
@@ -187,6 +192,25 @@ def gemm_run(plan: int, A, B, scales, C, workspace=None, stream=None) -> None:
                         _nbytes(workspace), stream)
     if st != GEMM_OK:
         raise GemmError(st, "gemm_run")
+
+
+def gemm_run_noalloc(plan: int, A, B, scales, C, stream=None) -> None:
+    """Enqueue C = A*B like gemm_run, with the library's own per-GPU split-K workspace
+    (GEMM_NOALLOC_WORKSPACE_BYTES) instead of a caller buffer: nothing is allocated. Calls
+    that overlap in time on one GPU share that workspace and must be serialised."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    need = _plan_bytes.get(plan)
+    if need is not None:
+        for x, n, what in ((A, need[0], "A"), (B, need[1], "B"), (scales, need[2], "scales"),
+                           (C, need[3], "C")):
+            _check_buffer(x, n, what)
+    st = lib().gemm_run_noalloc(plan, _ptr(A), _ptr(B), _ptr(scales), _ptr(C), stream)
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm_run_noalloc")
 
 
 def attn_fwd(Q, K, V, O, BH: int, Sq: int, Sk: int, D: int, dtype, scale: float,

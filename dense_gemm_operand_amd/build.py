@@ -26,7 +26,7 @@ COMMON = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument"]
 SOURCES = ["inst_f16.hip", "inst_bf16.hip", "inst_f8.hip", "inst_misc.hip", "inst_attn.hip",
-           "host.cpp"]
+           "noalloc.hip", "host.cpp"]
 
 
 def _compile(src: str, oversync: bool = False) -> str:

@@ -186,6 +186,24 @@ int gemm_workspace_size(gemm_plan_t plan, size_t* bytes);
 int gemm_run(gemm_plan_t plan, const void* A, const void* B, const void* scales, void* C,
              void* workspace, size_t ws_bytes, void* stream);
 
+/* Bytes of the per-GPU workspace that gemm_run_noalloc uses in place of a caller buffer. */
+#define GEMM_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)
+
+/* gemm_run for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same operation, arguments, layouts
+ * and results (bit for bit) as gemm_run, without the workspace arguments: a split-K plan
+ * uses a workspace of GEMM_NOALLOC_WORKSPACE_BYTES that the library holds in device memory
+ * of its own on each GPU it runs on (a static device array, reserved when the library's code
+ * is loaded on that GPU and held until the process ends). The first call on a GPU clears the
+ * arrival counters at its start with a small kernel on `stream`; every completed run leaves
+ * them zero again. No call allocates or frees memory.
+ * Calls on the same GPU share that one workspace: calls that overlap in time on one GPU
+ * (different streams, or different host threads) race and give wrong results; serialise them.
+ * Errors: as gemm_run, plus GEMM_ERR_WORKSPACE_TOO_SMALL when gemm_workspace_size exceeds
+ * GEMM_NOALLOC_WORKSPACE_BYTES, and GEMM_ERR_HIP when the device array cannot be resolved. */
+int gemm_run_noalloc(gemm_plan_t plan, const void* A, const void* B, const void* scales, void* C,
+                     void* stream);
+
 /* Copy the planner's choices into *info: the macro tile, the LDS padding and row
  * permutation of the operand tiles (rocm-libraries PR 2487, "Add support for permuting
  * perpDim" and LdsBlockSizePerPad under "Add support for m0 padding when using LDSTr+DTL"),

@@ -26,7 +26,8 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted([
         "gemm_plan", "gemm_workspace_size", "gemm_run", "gemm_plan_query",
-        "gemm_plan_destroy", "gemm_status_string", "gemm_lds_row_perm", "gemm_pack_u4_tiled"])
+        "gemm_plan_destroy", "gemm_status_string", "gemm_lds_row_perm", "gemm_pack_u4_tiled",
+        "gemm_run_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():

@@ -20,7 +20,8 @@ SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-f
 
 def _objects():
     objs = [os.path.join(PKG, "_build", f + ".o") for f in
-            ("inst_f16.hip", "inst_bf16.hip", "inst_f8.hip", "inst_misc.hip", "inst_attn.hip")]
+            ("inst_f16.hip", "inst_bf16.hip", "inst_f8.hip", "inst_misc.hip", "inst_attn.hip",
+             "noalloc.hip")]
     if not all(os.path.exists(o) for o in objs):
         from dense_gemm_operand_amd import build
         build.build(oversync=False)
