@@ -77,7 +77,9 @@ int find_variant(int kernel, const Plan& p, int tm, int tn, int perm) {
   for (int i = 0; i < variant_count(); ++i) {
     const VariantInfo& v = variant_info(i);
     if (kernel == KERNEL_TILE && waves > 0 && v.waves != waves) continue;
-    // DGEMM_FORCE_SCHED=<0|1> restricts tiled variants to one main-loop schedule (tuning).
+    // DGEMM_FORCE_SCHED=<0|1|2> restricts tiled variants to one main-loop schedule: 0 software
+    // pipeline, 1 two-group ping-pong, 2 four waves with every operand loaded straight into
+    // LDS (tuning, tests).
     const int sched = env_int("DGEMM_FORCE_SCHED", -1);
     if (kernel == KERNEL_TILE && sched >= 0 && v.sched != sched) continue;
     // DGEMM_FORCE_DTL=<0|1|2> restricts tiled variants to ones without direct-to-LDS loads,

@@ -55,6 +55,19 @@ def test_full_size_every_row_against_the_oracle(name, la, lb):
          f"(bound {4e-3 * np.sqrt(inp['K']) * amax * bmax:.3e})")
 
 
+def test_full_size_nonpow2_tile_every_row():
+    # the 3072 x 5120 x 6144 bf16 shape on the non-power-of-2 192 x 320 tile (16 x 16 = 256
+    # tiles for 256 CUs; the default plan takes 256 x 256), every row against the oracle
+    w = synth.WORKLOADS["nonpow2_bf16"]
+    _say("full nonpow2 192x320")
+    inp = synth.make_inputs(w)
+    c, info = run_gpu(inp, w.dtype_ab, w.dtype_c, split_k=1, force_tile="192x320", guard=16)
+    assert (info["tile_m"], info["tile_n"], info["grid_x"]) == (192, 320, 256)
+    amax, bmax = operand_max(inp, w.dtype_ab)
+    _, ref = reference(inp, w.dtype_ab, w.dtype_c)
+    check_tolerance(c, ref, w.dtype_c, inp["K"], amax, bmax, "192x320")
+
+
 def test_full_size_sampled_rows_int4_m4096():
     w = synth.WORKLOADS["int4_m4096"]
     _say("full sampled", w.name)

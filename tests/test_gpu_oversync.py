@@ -60,19 +60,21 @@ def _both(inp, fmt, out, hooks, split_k=1):
 LAYOUTS = [("col", "col"), ("col", "row"), ("row", "col"), ("row", "row")]
 # (schedule, loader): loader 0 = transposed operands through registers, 1 = K-contiguous
 # operands straight into LDS, 2 = transposed operands straight into LDS, transposed by the reads
-SCHED_LOADER = [(1, 1), (1, 2), (1, 0), (0, 0), (0, 1), (0, 2)]
+SCHED_LOADER = [(1, 1), (1, 2), (1, 0), (0, 0), (0, 1), (0, 2), (2, 1), (2, 2)]
 
 
-def _served(loader, la, lb):
+def _served(sched, loader, la, lb):
     transposed = la == "col" or lb == "row"
     kcontig = la == "row" or lb == "col"
+    if sched == 2:   # every operand direct: loader 1 for TN, loader 2 wherever one is transposed
+        return transposed if loader == 2 else (loader == 1 and not transposed)
     return {0: True, 1: kcontig, 2: transposed}[loader]
 
 
 @pytest.mark.parametrize("sched,loader", SCHED_LOADER)
 @pytest.mark.parametrize("la,lb", LAYOUTS)
 def test_oversynchronised_build_bit_identical(sched, loader, la, lb):
-    if not _served(loader, la, lb):
+    if not _served(sched, loader, la, lb):
         pytest.skip("this loader serves no operand of this layout pair")
     M, N, K = 520, 264, 712   # 3 x 2 tiles of 256 x 256, ragged edges, 11 K steps + a tail
     _say("oversync", sched, loader, la, lb)
