@@ -313,8 +313,10 @@ def loader_comparison(rounds: int = 5, calls: int = 20) -> list:
                 os.environ.pop("DGEMM_FORCE_DTL", None)
         d, alt = interleaved([hs[0].run, hs[1].run], rounds, calls)
         loader = lambda h: "transposing_lds_reads" if h.info["direct_lds"] & 12 else "in_register_transpose"
+        tile = lambda h: f"{h.info['tile_m']}x{h.info['tile_n']}"
         rec = {"workload": name, "layout_a": hs[0].la, "layout_b": hs[0].lb,
                "default": loader(hs[0]), "alternative": loader(hs[1]),
+               "default_tile": tile(hs[0]), "alternative_tile": tile(hs[1]),
                "alternative_us": round(alt * 1e3, 2),
                "alternative_over_default": round(alt / d, 4)}
         log(json.dumps(rec))
@@ -324,6 +326,39 @@ def loader_comparison(rounds: int = 5, calls: int = 20) -> list:
         del hs
         torch.cuda.empty_cache()
     return res
+
+
+def tile_comparison(rounds: int = 5, calls: int = 20) -> list:
+    """The 3072x5120x6144 bf16 shape on its default plan (the non-power-of-2 192x320 tile:
+    256 tiles, 8-wave ping-pong with 16x16x32 blocks, every operand straight into LDS)
+    against 240 tiles of 256x256 on the 8-wave ping-pong with 32x32x16 blocks (planner hook
+    DGEMM_FORCE_TILE=256x256), timed interleaved. The default's own time is the one under
+    "workloads"; here only the alternative's time and the ratio appear."""
+    import torch
+    from dense_gemm_operand_amd import synth
+    wl = synth.WORKLOADS["nonpow2_bf16"]
+    hs = []
+    for tile in (None, "256x256"):
+        if tile is not None:
+            os.environ["DGEMM_FORCE_TILE"] = tile
+        try:
+            hs.append(Gemm(wl))
+        finally:
+            os.environ.pop("DGEMM_FORCE_TILE", None)
+    d, alt = interleaved([hs[0].run, hs[1].run], rounds, calls)
+    desc = lambda h: (f"{h.info['tile_m']}x{h.info['tile_n']}, {h.info['waves']} waves, "
+                      f"schedule {h.info['schedule']}, {h.info['mfma_m']}x{h.info['mfma_m']} "
+                      f"blocks, direct_lds {h.info['direct_lds']}, grid {h.info['grid_x']}")
+    rec = {"workload": wl.name, "layout_a": hs[0].la, "layout_b": hs[0].lb,
+           "default": desc(hs[0]), "alternative": desc(hs[1]),
+           "alternative_us": round(alt * 1e3, 2),
+           "alternative_over_default": round(alt / d, 4)}
+    log(json.dumps(rec))
+    for h in hs:
+        h.close()
+    del hs
+    torch.cuda.empty_cache()
+    return [rec]
 
 
 def _vendor_mm(h: "Gemm"):
@@ -622,7 +657,8 @@ def main():
                    "loader": ("transposing LDS reads" if h.info["direct_lds"] & 12 else
                               "in-register transpose" if (h.la == "col" or h.lb == "row") else
                               "K-contiguous"),
-                   "direct_lds": h.info["direct_lds"], "waves": h.info["waves"]}
+                   "direct_lds": h.info["direct_lds"], "waves": h.info["waves"],
+                   "schedule": h.info["schedule"], "mfma_m": h.info["mfma_m"]}
             peak = PEAK_F8_TFLOPS if wl.dtype_ab == "f8" else PEAK_TFLOPS
             rec["pct_peak"] = round(100 * (rec["tflops"] / peak if bound == "mfma"
                                            else rec["gbs"] / PEAK_GBS), 2)
@@ -650,6 +686,7 @@ def main():
                          "pair on the launch stream (HIP graph replays for kernels under 50 "
                          "us); the comparisons below give ratios from interleaved batches")
         out["loader_comparison"] = loader_comparison()
+        out["tile_comparison"] = tile_comparison()
         out["int4_layout_comparison"] = int4_layout_comparison()
         out["vendor_blas_comparison"] = vendor_blas_comparison()
         out["context"] = stream_context()

@@ -60,7 +60,8 @@ class gemm_plan_info_t(ctypes.Structure):
                 ("grid_y", ctypes.c_int64), ("grid_z", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64), ("lds_bytes", ctypes.c_int32),
                 ("cu_count", ctypes.c_int32), ("slots_per_cu", ctypes.c_int32),
-                ("direct_lds", ctypes.c_int32), ("schedule", ctypes.c_int32)]
+                ("direct_lds", ctypes.c_int32), ("schedule", ctypes.c_int32),
+                ("mfma_m", ctypes.c_int32)]
 
 
 _lib = None

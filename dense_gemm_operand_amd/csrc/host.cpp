@@ -86,6 +86,9 @@ int find_variant(int kernel, const Plan& p, int tm, int tn, int perm) {
     // with them for K-contiguous operands only, or with them for transposed operands too
     // (transposed by the LDS reads) (tuning, tests).
     const int dtl = env_int("DGEMM_FORCE_DTL", -1);
+    // DGEMM_FORCE_MFMA=<32|16> restricts tiled variants to one matrix-core block (tests).
+    const int mfma = env_int("DGEMM_FORCE_MFMA", 0);
+    if (kernel == KERNEL_TILE && mfma > 0 && v.mfma != mfma) continue;
     const int have = (v.dtl & 12) ? 2 : (v.dtl ? 1 : 0);
     if (kernel == KERNEL_TILE && dtl >= 0 && have != dtl) continue;
     if (v.kernel != kernel || v.dtype_a != p.dtype_a || v.dtype_b != p.dtype_b) continue;
@@ -173,10 +176,12 @@ int make_plan(Plan& p, int split_k_req) {
   if (v.kernel == KERNEL_TILE && v.perm == 2) p.lds_pad = 0;  // unpadded comparison variant
   if (p.direct_lds & 12) {
     // transposed operands in global order: 64 bytes of padding per 1 KiB LDS block and the
-    // K-row permutation B = 8, S = 4
+    // K-row permutation B = 8, S = 4 (256-wide tiles, two K rows per block) or B = 64,
+    // S = 8 (other widths, eight 64-wide K-row segments per block)
+    const int tr_rows = (p.direct_lds & 4) ? p.tile_m : p.tile_n;
     p.lds_pad = 64;
-    p.perm_block = 8;
-    p.perm_stride = 4;
+    p.perm_block = tr_rows == 256 ? 8 : 64;
+    p.perm_stride = tr_rows == 256 ? 4 : 8;
   }
   if (v.kernel == KERNEL_SKINNY) {
     p.lds_pad = 0;
@@ -374,6 +379,7 @@ int gemm_plan_query(gemm_plan_t plan, gemm_plan_info_t* info) {
   info->slots_per_cu = p.slots_per_cu;
   info->direct_lds = p.direct_lds;
   info->schedule = p.kernel == dg::KERNEL_TILE ? dg::variant_info(p.variant).sched : 0;
+  info->mfma_m = dg::variant_info(p.variant).mfma;
   return GEMM_OK;
 }
 

@@ -16,12 +16,20 @@ static const Variant kTable[] = {
     TILE_LAYOUTS_DTL(BF16T, 256, 256, 2, 4),
     TILE_LAYOUTS(BF16T, 256, 256, 2, 4),
     TILE_LAYOUTS(BF16T, 256, 256, 2, 2),
+    // the non-power-of-2 192x320 tile (16 x 16 tiles for a 3072 x 5120 C on 256 CUs): first
+    // the 8-wave ping-pong with 16x16x32 blocks (96x80 per wave) and every operand straight
+    // into LDS (transposed ones in 64-wide K-row segments), then schedule 2 (4 waves), the
+    // register-staged pipeline and the pipeline with direct loads
+    TILE_LAYOUTS_PP16(BF16T, 192, 320),
+    TILE_LAYOUTS_W4(BF16T, 192, 320),
     TILE_LAYOUTS(BF16T, 192, 320, 2, 2),
+    TILE_LAYOUTS_DTL(BF16T, 192, 320, 2, 2),
+    TILE_LAYOUTS_DTLTR(BF16T, 192, 320, 2, 2),
     TILE_LAYOUTS(BF16T, 128, 128, 2, 2),
     TILE_LAYOUTS(BF16T, 64, 64, 2, 2),
     TILE_LAYOUTS_DTL(BF16T, 256, 256, 2, 2),
     TILE_LAYOUTS_DTLTR(BF16T, 256, 256, 2, 4),
-    TILE_LAYOUTS_W4(BF16T),
+    TILE_LAYOUTS_W4(BF16T, 256, 256),
 };
 
 int variants_bf16(const Variant** out) {

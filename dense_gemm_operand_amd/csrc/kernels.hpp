@@ -480,30 +480,52 @@ struct DtlOperand {
   }
 };
 
-// An operand whose contiguous index is M or N (256 of them per tile), moved by direct
-// global->LDS loads and transposed on the read instead of in registers (rocm-libraries
-// PR 2487: direct-to-LDS with padding per LDS block and a permutation of the perpendicular
-// dimension). LDS keeps global order: each K row is 256 contiguous M (or N) values, 512 B.
-// One load instruction of a wave fills a 1 KiB block (two K rows; lane t: row t/32,
-// elements 8(t%32)..+7), followed by 64 bytes of padding. Within each group of eight K rows
-// the rows are placed with the page's permutation, B = 8, S = 4: LDS row L of the group
-// holds K row fwd(L) = 4(L%2) + L/2, so block j holds K rows j and j+4.
+// An operand whose contiguous index is M or N (ROWS of them per tile, a multiple of 64),
+// moved by direct global->LDS loads and transposed on the read instead of in registers
+// (rocm-libraries PR 2487: direct-to-LDS with padding per LDS block and a permutation of the
+// perpendicular dimension, for power-of-2 and other macro tiles alike). Every load
+// instruction of a wave fills one 1 KiB LDS block, followed by 64 bytes of padding (the pad
+// goes in through the per-instruction LDS base, as the page's m0 padding). Each lane moves
+// 16 bytes, so the divisions that map a lane to its K row and M chunk are by powers of 2 for
+// any ROWS.
 // ds_read_b64_tr_b16 (gfx950) gives lane t of each 16-lane group element t%4 of the 8-byte
 // chunks addressed by lanes t/4 + 4e, e = 0..3. Reading, per 16-lane group, K rows
-// kb + 4r + s/4 (block s/4 of the group, half r) at M chunk s%4 (s = lane%16) gives lane t
-// M index t and the four K values kb + 4r .. kb + 4r + 3; two reads (r = 0, 1) make one
-// v_mfma_f32_32x32x16 fragment in natural K order. The four rows read by a half-wave lie
-// in four consecutive blocks, 1088 B apart, i.e. at bank offsets 0, 64, 128 and 192 B, so
-// the reads are free of bank conflicts.
+// kb + 4r + s/4 at M chunk s%4 (s = lane%16) gives lane t M index t and the four K values
+// kb + 4r .. kb + 4r + 3; two reads (r = 0, 1) make one v_mfma_f32_32x32x16 fragment in
+// natural K order. Lanes 32..63 read K rows kb + 8 .. kb + 15.
+// Two block layouts, both free of bank conflicts for these reads (the four K rows a
+// half-wave reads lie in four consecutive blocks at the same in-block offset, 1088 B apart,
+// i.e. at bank offsets 0, 64, 128 and 192 B):
+//  - ROWS == 256 (ROWS-wide K rows, 512 B): a block holds two K rows (lane t: row t/32,
+//    elements 8(t%32)..+7). Within each group of eight K rows the rows are placed with the
+//    page's permutation B = 8, S = 4: LDS row L of the group holds K row 4(L%2) + L/2, so
+//    block j holds K rows j and j+4.
+//  - other ROWS (192, 320, ...: the non-power-of-2 macro tiles): the tile is cut into
+//    64-wide segments and a block holds eight 128-byte K rows of one segment (lane t: row
+//    i = t/8, LDS chunk t%8, whole 128-byte lines of global memory). The 64 K rows of a
+//    step are placed with the page's permutation B = 64, S = 8: LDS row I = 8b + i (block b
+//    of the segment, row i) holds K row 8i + b, so consecutive K rows go to consecutive
+//    blocks, i.e. to different load instructions, and the m0 padding separates their banks.
+//    In odd rows the 16-byte chunks of a segment are stored with chunk c at position c ^ 2.
+//    A 32x32x16 fragment read (two 16-lane groups on the same four rows, 32 M values)
+//    never pairs an odd row with an even one; for the 16x16x32 reads (16 M values, the two
+//    16-lane groups of a half-wave on rows i and i + 1 of the same four blocks, 128 B
+//    apart) the swap moves the odd row's 32 bytes to the other half of the same 64-byte
+//    bank group, so both shapes read free of bank conflicts.
 template <int ROWS, int THREADS>
 struct DtlTrOperand {
-  static_assert(ROWS == 256, "two 512-byte K rows per 1 KiB load");
+  static_assert(ROWS % 64 == 0, "whole 64-wide segments");
+  static constexpr bool SEG = ROWS != 256;
   static constexpr int WAVES = THREADS / 64;
-  static constexpr int BLOCKS = 32;               // 64 K rows per step, two per block
+  static constexpr int BLOCKS = ROWS / 8;         // 64 K rows x ROWS x 2 B per step, 1 KiB each
   static constexpr int NI = BLOCKS / WAVES;       // load instructions per wave and K step
   static constexpr int BLOCK_BYTES = 1024 + 64;   // data + padding
   static constexpr int BYTES = BLOCKS * BLOCK_BYTES;
-  static constexpr RowPerm P = RowPerm{8, 4};
+  static constexpr RowPerm P = SEG ? RowPerm{64, 8} : RowPerm{8, 4};
+  // Byte distances between the reads of one fragment (r = 1 against r = 0) and between
+  // 16-K sub-steps.
+  static constexpr int R1 = SEG ? 4 * BLOCK_BYTES : 512;
+  static constexpr int KK_BYTES = SEG ? 256 : 8 * BLOCK_BYTES;
   static_assert(BLOCKS % WAVES == 0, "whole blocks per wave");
   uint32_t off[NI];  // byte offsets at the split's first K step (kOOB outside the operand)
   int krow[NI];      // K row of the lane, relative to the step start
@@ -512,9 +534,16 @@ struct DtlTrOperand {
                                         int kb) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int b = wave * NI + j;                        // block: group b/4, slot b%4
-      const int k = 8 * (b / 4) + P.fwd(2 * (b % 4) + lane / 32);
-      const int m = row0 + 8 * (lane % 32);
+      const int b = wave * NI + j;
+      int k, m;
+      if constexpr (SEG) {   // block b: segment b/8, K rows P.fwd(8(b%8) + i), i = row in block
+        const int i = lane / 8;
+        k = P.fwd(8 * (b % 8) + i);
+        m = row0 + 64 * (b / 8) + 8 * ((lane % 8) ^ (2 * (i & 1)));
+      } else {               // block b: group b/4, slot b%4
+        k = 8 * (b / 4) + P.fwd(2 * (b % 4) + lane / 32);
+        m = row0 + 8 * (lane % 32);
+      }
       off[j] = m < rows_total ? (uint32_t)((kb + k) * ld + m) * 2u : kOOB;
       krow[j] = k;
     }
@@ -534,22 +563,43 @@ struct DtlTrOperand {
         : "v"(o), "s"(m0v), "s"(rs)
         : "memory", "m0");
   }
-  // Lane's byte offset (stage-relative) for sub-step 0, read 0, fragment block 0, of the
-  // wave's rows starting at wrow; sub-step kk adds 8 * BLOCK_BYTES * kk, read 1 adds 512,
-  // fragment block i (32 rows) adds 64 i.
-  __device__ __forceinline__ static int read_base(int lane, int wrow) {
+  // LDS byte offset (stage-relative) of M (or N) index m of the K row that is row i of
+  // block b of m's segment (segment layout).
+  __device__ __forceinline__ static int seg_off(int b, int i, int m) {
+    return (8 * (m / 64) + b) * BLOCK_BYTES + i * 128 + ((((m % 64) / 8) ^ (2 * (i & 1))) * 16) +
+           (m % 8) * 2;
+  }
+  // Lane's byte offset (stage-relative) of the 32x32x16 fragment whose 32 M (or N) indices
+  // start at col (a multiple of 32), for sub-step 0 and read 0; sub-step kk adds
+  // KK_BYTES * kk, read 1 adds R1.
+  __device__ __forceinline__ static int frag_off(int lane, int col) {
     const int G = lane / 16, s = lane % 16;
-    return (4 * (G / 2) + s / 4) * BLOCK_BYTES + (16 * (G % 2) + 4 * (s % 4)) * 2 + wrow * 2;
+    const int m = col + 16 * (G % 2) + 4 * (s % 4);
+    if constexpr (SEG)
+      return seg_off(s / 4, G / 2, m);
+    else
+      return (4 * (G / 2) + s / 4) * BLOCK_BYTES + m * 2;
+  }
+  // The same for a 16x16x32 fragment (16 M or N indices from col, a multiple of 16; lane
+  // group G = lane/16 takes K rows 8G .. 8G + 7 of the 32-K half step): half step h adds
+  // KK16_BYTES * h, read 1 adds R1. Segment layout only (in the two-row layout the eight
+  // blocks a half-wave reads would meet in pairs on the same banks).
+  static constexpr int KK16_BYTES = 4 * 128;
+  __device__ __forceinline__ static int frag_off16(int lane, int col) {
+    static_assert(SEG, "16x16x32 fragments: segment layout");
+    const int G = lane / 16, s = lane % 16;
+    return seg_off(s / 4, G, col + 4 * (s % 4));
   }
 };
 
-// One v_mfma_f32_32x32x16 fragment from a transposed LDS block: reads at p and p + 512.
+// One v_mfma_f32_32x32x16 fragment from a transposed LDS block: reads at p and p + R1.
+template <int R1>
 __device__ __forceinline__ u32x4 tr_fragment(const char* p) {
   typedef short v4i16 __attribute__((ext_vector_type(4)));
   const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) v4i16*)p);
   const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16*)(p + 512));
+      (__attribute__((address_space(3))) v4i16*)(p + R1));
   const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
   return u32x4{a[0], a[1], b[0], b[1]};
 }
@@ -557,15 +607,19 @@ __device__ __forceinline__ u32x4 tr_fragment(const char* p) {
 // LROWS, the LDS rows of operands stored by the threads: 1 = permuted (transposed operands)
 // and padded, 0 = identity order and padded, 2 = identity order without padding. 0 and 2
 // are comparison variants for bank-conflict measurements.
+// MI: the matrix-core block, 32 (v_mfma_f32_32x32x16, fp8 32x32x64) or 16
+// (v_mfma_f32_16x16x32; the 8-wave tiles whose wave tiles are not whole 32x32 blocks, e.g.
+// 96x80 in 192x320).
 template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN,
-          int LROWS, int DTL>
+          int LROWS, int DTL, int MI = 32>
 struct TileCfg {
   static constexpr int EB = elem_bytes<T>();
   static constexpr bool F8 = EB == 1;
   static constexpr int BK = 128 / EB;                    // K per step: 128-byte LDS rows
   static constexpr int THREADS = WM * WN * 64;
   static constexpr int WT_M = MT_M / WM, WT_N = MT_N / WN;
-  static constexpr int TM = WT_M / 32, TN = WT_N / 32;   // 32x32 blocks per wave
+  static constexpr int TM = WT_M / MI, TN = WT_N / MI;   // MIxMI blocks per wave
+  static_assert(MI == 32 || MI == 16, "matrix-core block");
   // Direct-to-LDS loads (DTL >= 1) for K-contiguous operands (not for int4 codes, which
   // are dequantised in registers); with DTL == 2 also for the transposed operands, which
   // are then transposed by the LDS reads instead of in registers.
@@ -605,7 +659,11 @@ struct TileCfg {
   // owns more than four blocks, where the second set would not fit in the register file.
   static constexpr int NSETS = (SA + SB) > 4 ? 1 : 2;
   static_assert(!ANY_DTL || NSETS == 2, "direct-to-LDS schedule keeps loads a step ahead");
-  static_assert(WT_M % 32 == 0 && WT_N % 32 == 0, "wave tile must be whole 32x32 blocks");
+  static_assert(WT_M % MI == 0 && WT_N % MI == 0, "wave tile must be whole MIxMI blocks");
+  // 16x16x32 blocks: 16-bit operands, every operand straight into LDS (the direct epilogue
+  // assumes LDS rows in logical order)
+  static_assert(MI == 32 || (!F8 && !U4B && SA == 0 && SB == 0 && PA.block == 1 && PB.block == 1),
+                "16x16x32 blocks: 16-bit operands loaded straight into LDS");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -661,9 +719,10 @@ constexpr bool epilogue_runs16_ok() {
 }
 
 template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN,
-          int LROWS, int SCHED, int DTL>
+          int LROWS, int SCHED, int DTL, int MI>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
-  using Cfg = TileCfg<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, LROWS, DTL>;
+  using Cfg = TileCfg<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, LROWS, DTL, MI>;
+  static_assert(MI == 32 || SCHED == 1, "16x16x32 blocks: ping-pong schedule");
   using OpA = typename Cfg::OpA;
   using OpB = typename Cfg::OpB;
   constexpr int BK = Cfg::BK, THREADS = Cfg::THREADS;
@@ -821,11 +880,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     }
   };
 
-  f32x16 acc[TM * TN];
+  // accumulators: one 32x32 (16 floats per lane) or 16x16 (4 floats per lane) block each
+  using AccT = std::conditional_t<MI == 16, f32x4, f32x16>;
+  constexpr int ACC_LEN = MI == 16 ? 4 : 16;
+  AccT acc[TM * TN];
 #pragma unroll
   for (int i = 0; i < TM * TN; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+    for (int e = 0; e < ACC_LEN; ++e) acc[i][e] = 0.f;
 
   // Fragment reads (v_mfma_f32_32x32x16): lane reads LDS row (32-row block base +
   // lane%32), 16-byte chunk 2*kk + lane/32 of the step's K sub-step kk.
@@ -839,9 +901,31 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     a_rd[kk] = (wm * Cfg::WT_M + r32) * PA16 + ca;
     b_rd[kk] = Cfg::A16 + (wn * Cfg::WT_N + r32) * PB16 + cb;
   }
-  // Transposed direct-to-LDS operands: byte offsets of the transposing reads.
-  const int a_tr = Cfg::TA::read_base(lane, wm * Cfg::WT_M);
-  const int b_tr = Cfg::A16 * 16 + Cfg::TB::read_base(lane, wn * Cfg::WT_N);
+  // 16x16x32 fragments: lane reads LDS row (16-row block base + lane%16), 16-byte chunk
+  // 4h + lane/16 of the step's 32-K half h; block i adds 16 rows.
+  const int r16 = lane & 15, kq = lane >> 4;
+  int a_rd16[2], b_rd16[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int ca = Cfg::A_DTL ? ((4 * h + kq) ^ dtl_swz(r16)) : 4 * h + kq;
+    const int cb = Cfg::B_DTL ? ((4 * h + kq) ^ dtl_swz(r16)) : 4 * h + kq;
+    a_rd16[h] = (wm * Cfg::WT_M + r16) * PA16 + ca;
+    b_rd16[h] = Cfg::A16 + (wn * Cfg::WT_N + r16) * PB16 + cb;
+  }
+  // Transposed direct-to-LDS operands: byte offsets of the transposing reads, per block.
+  int a_tr[TM], b_tr[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    if constexpr (MI == 16 && Cfg::A_TR) a_tr[i] = Cfg::TA::frag_off16(lane, wm * Cfg::WT_M + 16 * i);
+    else a_tr[i] = Cfg::TA::frag_off(lane, wm * Cfg::WT_M + 32 * i);
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    if constexpr (MI == 16 && Cfg::B_TR)
+      b_tr[j] = Cfg::A16 * 16 + Cfg::TB::frag_off16(lane, wn * Cfg::WT_N + 16 * j);
+    else
+      b_tr[j] = Cfg::A16 * 16 + Cfg::TB::frag_off(lane, wn * Cfg::WT_N + 32 * j);
+  }
 
   // Instruction counts of one sub-step, for the interleaving below.
   constexpr int N_MFMA = TM * TN;
@@ -868,16 +952,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         if constexpr (Cfg::A_TR)
-          fa[kk & 1][i] = tr_fragment(reinterpret_cast<const char*>(st) + a_tr +
-                                      8 * Cfg::TA::BLOCK_BYTES * kk + 64 * i);
+          fa[kk & 1][i] = tr_fragment<Cfg::TA::R1>(reinterpret_cast<const char*>(st) + a_tr[i] +
+                                                   Cfg::TA::KK_BYTES * kk);
         else
           fa[kk & 1][i] = st[a_rd[kk] + i * 32 * PA16];
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         if constexpr (Cfg::B_TR)
-          fb[kk & 1][j] = tr_fragment(reinterpret_cast<const char*>(st) + b_tr +
-                                      8 * Cfg::TB::BLOCK_BYTES * kk + 64 * j);
+          fb[kk & 1][j] = tr_fragment<Cfg::TB::R1>(reinterpret_cast<const char*>(st) + b_tr[j] +
+                                                   Cfg::TB::KK_BYTES * kk);
         else
           fb[kk & 1][j] = st[b_rd[kk] + j * 32 * PB16];
       }
@@ -897,11 +981,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
       }
       constexpr int n_vmem = NS == 2 ? N_VMEM : (kk == 0 ? 4 * N_VMEM : 0);
       constexpr int n_write = NS == 2 ? N_WRITE : (kk >= 2 ? 2 * N_WRITE : 0);
+      if constexpr (MI == 32) {   // (the 16x16x32 kernels run the ping-pong schedule only)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i * TN + j] = mfma32x32x16<T>(fb[kk & 1][j], fa[kk & 1][i], acc[i * TN + j]);
+          for (int j = 0; j < TN; ++j)
+            acc[i * TN + j] = mfma32x32x16<T>(fb[kk & 1][j], fa[kk & 1][i], acc[i * TN + j]);
+      }
       // one matrix-core instruction, then a share of the other work, repeated
 #pragma unroll
       for (int g = 0; g < N_MFMA; ++g) {
@@ -966,7 +1052,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
       fb[j][0] = st[b_rd[2 * H] + j * 32 * PB16];
       fb[j][1] = st[b_rd[2 * H + 1] + j * 32 * PB16];
     };
-    auto mma = [&](int i, int j) { acc[i * TN + j] = mfma32x32x64_f8(fb[j], fa[i], acc[i * TN + j]); };
+    auto mma = [&](int i, int j) {
+      if constexpr (MI == 32) acc[i * TN + j] = mfma32x32x64_f8(fb[j], fa[i], acc[i * TN + j]);
+    };
     // Slot g of a half: one multiply, then that slot's share of the stores and loads.
     auto slots = [&](auto H_) {
       constexpr int H = decltype(H_)::value;
@@ -1072,7 +1160,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     constexpr int NIA = Cfg::A_DTL ? Cfg::DA::NI : (Cfg::A_TR ? Cfg::TA::NI : 0);
     constexpr int NIB = Cfg::B_DTL ? Cfg::DB::NI : (Cfg::B_TR ? Cfg::TB::NI : 0);
     constexpr int NLD = NIA + NIB;   // direct loads per wave and step
-    static_assert(NLD == TM * TN, "one direct load per multiply of sub-step 3");
+    constexpr int NMF = TM * TN;     // multiplies per sub-step
     u32x4 fa[2][TM], fb[2][TN];
     auto read_frag = [&](int buf, int kk, int q, int f) {
       // fragment f of sub-step kk: A blocks 0..TM-1, then B blocks 0..TN-1
@@ -1081,13 +1169,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
       if (f < TM) {
         const int i = f;
         if constexpr (Cfg::A_TR)
-          fa[q][i] = tr_fragment(sbytes + a_tr + 8 * Cfg::TA::BLOCK_BYTES * kk + 64 * i);
+          fa[q][i] = tr_fragment<Cfg::TA::R1>(sbytes + a_tr[i] + Cfg::TA::KK_BYTES * kk);
         else
           fa[q][i] = st[a_rd[kk] + i * 32 * PA16];
       } else {
         const int j = f - TM;
         if constexpr (Cfg::B_TR)
-          fb[q][j] = tr_fragment(sbytes + b_tr + 8 * Cfg::TB::BLOCK_BYTES * kk + 64 * j);
+          fb[q][j] = tr_fragment<Cfg::TB::R1>(sbytes + b_tr[j] + Cfg::TB::KK_BYTES * kk);
         else
           fb[q][j] = st[b_rd[kk] + j * 32 * PB16];
       }
@@ -1105,7 +1193,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     };
     // Sub-step kk of a step in buffer CUR: multiply set Q, and after the multiply g, read
     // fragment g of the next sub-step (from buffer RBUF, sub-step RKK, into set Q ^ 1) and,
-    // in sub-step 3, issue direct load g of step s + 2 into buffer CUR.
+    // in sub-step 3, issue the direct loads of step s + 2 into buffer CUR (load l after
+    // multiply l * NMF / NLD).
     auto substep = [&](int s, auto CUR_, auto KK_) {
       constexpr int CUR = decltype(CUR_)::value, kk = decltype(KK_)::value;
       constexpr int Q = kk & 1;
@@ -1115,7 +1204,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
         const int i = g / TN, j = g % TN;
         acc[i * TN + j] = mfma32x32x16<T>(fb[Q][j], fa[Q][i], acc[i * TN + j]);
         if (g < TM + TN) read_frag(RBUF, RKK, Q ^ 1, g);
-        if constexpr (kk == 3) dtl_one(s + 2, CUR, g);
+        if constexpr (kk == 3) {
+          // the step's direct loads spread evenly over the sub-step's multiplies
+#pragma unroll
+          for (int l = g * NLD / NMF; l < (g + 1) * NLD / NMF; ++l) dtl_one(s + 2, CUR, l);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -1174,26 +1267,49 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
       constexpr int H = decltype(H_)::value;
       const u32x4* st = lds + buf * Cfg::STAGE16;
       const char* sbytes = reinterpret_cast<const char*>(st);
+      if constexpr (MI == 16) {   // one 16x16x32 fragment per block covers the half
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          if constexpr (Cfg::A_TR)
+            fa[0][i] = tr_fragment<Cfg::TA::R1>(sbytes + a_tr[i] + Cfg::TA::KK16_BYTES * H);
+          else
+            fa[0][i] = st[a_rd16[H] + i * 16 * PA16];
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          if constexpr (Cfg::B_TR)
+            fb[0][j] = tr_fragment<Cfg::TB::R1>(sbytes + b_tr[j] + Cfg::TB::KK16_BYTES * H);
+          else
+            fb[0][j] = st[b_rd16[H] + j * 16 * PB16];
+        }
+        return;
+      }
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
           if constexpr (Cfg::A_TR)
-            fa[q][i] = tr_fragment(sbytes + a_tr + 8 * Cfg::TA::BLOCK_BYTES * (2 * H + q) + 64 * i);
+            fa[q][i] = tr_fragment<Cfg::TA::R1>(sbytes + a_tr[i] + Cfg::TA::KK_BYTES * (2 * H + q));
           else
             fa[q][i] = st[a_rd[2 * H + q] + i * 32 * PA16];
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           if constexpr (Cfg::B_TR)
-            fb[q][j] = tr_fragment(sbytes + b_tr + 8 * Cfg::TB::BLOCK_BYTES * (2 * H + q) + 64 * j);
+            fb[q][j] = tr_fragment<Cfg::TB::R1>(sbytes + b_tr[j] + Cfg::TB::KK_BYTES * (2 * H + q));
           else
             fb[q][j] = st[b_rd[2 * H + q] + j * 32 * PB16];
         }
       }
     };
     auto compute = [&]() {
-      if constexpr (Cfg::F8) {
+      if constexpr (MI == 16) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i * TN + j] = mfma16x16x32<T>(fb[0][j], fa[0][i], acc[i * TN + j]);
+      } else if constexpr (Cfg::F8) {
         // one 32x32x64 multiply per block and half: its 32-byte fragment is the half's two
         // 16-byte chunks, read as for the two 16-bit sub-steps (same chunks on A and B, so
         // the products pair up as in the fp8 pipeline step)
@@ -1309,7 +1425,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   // the fix-up's element-wise sums)
   if constexpr (SCHED != 2) {
     if (sk > 1) {
-      if (!splitk_fixup<f32x16, TM * TN, THREADS>(acc, a, tile, z, sk, tiles)) return;
+      if (!splitk_fixup<AccT, TM * TN, THREADS>(acc, a, tile, z, sk, tiles)) return;
     }
   }
 
@@ -1343,7 +1459,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int nb = wn * Cfg::WT_N + j * 32 + 8 * g + 4 * kh;
-            const f32x16& v = acc[i * TN + j];
+            const auto& v = acc[i * TN + j];   // (a 32x32 block: 16 floats)
             if constexpr (PB.block == 1) {
               O* dst = reinterpret_cast<O*>(cl + (m - lo) * CP + nb * OB);
               typedef O o4 __attribute__((ext_vector_type(4)));
@@ -1367,7 +1483,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
               if (j == 0 && g < 2) {
                 // LDS rows nb + e + 16t, t = 2j' + g' (block j', group g + 2g'), hold the
                 // logical columns fwd_B(nb + e) + t: one vector store per e.
-                const f32x16& v1 = acc[i * TN + 1];
+                const auto& v1 = acc[i * TN + 1];
                 typedef O o4 __attribute__((ext_vector_type(4)));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -1410,11 +1526,35 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   // cover 16 contiguous bytes of 32 rows (fp16), and the 16 stores of a block fill whole
   // 128-byte lines of those rows. No LDS round trip, and no accumulator needs to wait for a
   // second pass (the two-pass LDS epilogue of an fp32 tile would not fit the registers).
+  // The 16x16x32 kernels do the same: lane l of block (i, j) holds row 16i + l%16 and the
+  // four consecutive columns 16j + 4(l/16) + 0..3 (operands in logical order in LDS).
   auto epilogue_direct = [&](auto dt_tag) {
     constexpr int DT = decltype(dt_tag)::value;
     using O = typename OutT<DT>::type;
     typedef O o4 __attribute__((ext_vector_type(4)));
     O* Cg = reinterpret_cast<O*>(a.C);
+    if constexpr (MI == 16) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int gm = m0 + wm * Cfg::WT_M + i * 16 + r16;
+        if (gm >= a.M) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int gn = n0 + wn * Cfg::WT_N + j * 16 + 4 * kq;
+          const f32x4& v = acc[i * TN + j];
+          O* dst = Cg + (size_t)gm * a.N + gn;
+          if (a.c_vec && gn + 4 <= a.N) {
+            o4 w = {cvt_out<DT>(v[0]), cvt_out<DT>(v[1]), cvt_out<DT>(v[2]), cvt_out<DT>(v[3])};
+            *reinterpret_cast<o4*>(dst) = w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (gn + e < a.N) dst[e] = cvt_out<DT>(v[e]);
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int gm = m0 + wm * Cfg::WT_M + i * 32 + r32;
@@ -1424,7 +1564,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int gn = n0 + wn * Cfg::WT_N + j * 32 + 8 * g + 4 * kh;
-          const f32x16& v = acc[i * TN + j];
+          const auto& v = acc[i * TN + j];
           O* dst = Cg + (size_t)gm * a.N + gn;
           if (a.c_vec && gn + 4 <= a.N) {
             o4 w = {cvt_out<DT>(v[4 * g]), cvt_out<DT>(v[4 * g + 1]), cvt_out<DT>(v[4 * g + 2]),
@@ -1439,16 +1579,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
       }
     }
   };
-  if constexpr (SCHED == 2) {
+  if constexpr (SCHED == 2 || MI == 16) {
     if (a.dtype_c == DT_F16) epilogue_direct(std::integral_constant<int, DT_F16>{});
     else if (a.dtype_c == DT_BF16) epilogue_direct(std::integral_constant<int, DT_BF16>{});
     else epilogue_direct(std::integral_constant<int, DT_F32>{});
-    return;
+  } else {
+    // The C tile reuses the operand LDS: every wave is past the loop's last barrier.
+    if (a.dtype_c == DT_F16) epilogue(std::integral_constant<int, DT_F16>{});
+    else if (a.dtype_c == DT_BF16) epilogue(std::integral_constant<int, DT_BF16>{});
+    else epilogue(std::integral_constant<int, DT_F32>{});
   }
-  // The C tile reuses the operand LDS: every wave is past the loop's last barrier.
-  if (a.dtype_c == DT_F16) epilogue(std::integral_constant<int, DT_F16>{});
-  else if (a.dtype_c == DT_BF16) epilogue(std::integral_constant<int, DT_BF16>{});
-  else epilogue(std::integral_constant<int, DT_F32>{});
 }
 
 // ================================================================= skinny kernel
@@ -1679,11 +1819,11 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny_kernel(KArgs a) {
 using LaunchFn = hipError_t (*)(const Plan&, const KArgs&, hipStream_t);
 
 template <class T, bool A_KC, bool B_KC, bool U4B, int MT_M, int MT_N, int WM, int WN, int LROWS,
-          int PP, int DTL>
+          int PP, int DTL, int MI>
 hipError_t launch_tile(const Plan& p, const KArgs& a, hipStream_t s) {
-  using Cfg = TileCfg<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, LROWS, DTL>;
+  using Cfg = TileCfg<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, LROWS, DTL, MI>;
   dim3 grid((unsigned)p.grid_x, (unsigned)p.grid_y, (unsigned)p.grid_z);
-  hipLaunchKernelGGL((gemm_tile_kernel<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, LROWS, PP, DTL>),
+  hipLaunchKernelGGL((gemm_tile_kernel<T, A_KC, B_KC, U4B, MT_M, MT_N, WM, WN, LROWS, PP, DTL, MI>),
                      grid, dim3(Cfg::THREADS), 0, s, a);
   return hipGetLastError();
 }
@@ -1704,17 +1844,18 @@ struct Variant {
   LaunchFn fn;
 };
 
-#define TILE_X(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, PP, DTL)                            \
+#define TILE_XM(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, PP, DTL, MI)                       \
   Variant{VariantInfo{KERNEL_TILE, dt_code<T>(), (U4) ? DT_U4 : dt_code<T>(), (AKC) ? 0 : 1,  \
                       (BKC) ? 1 : 0, MTM, MTN,                                               \
-                      TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::BK, (WM) * (WN), 1, PERM, \
-                      TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::lds_alloc(PP),  \
-                      TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::NSETS, 1, PP,   \
-                      (TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::A_DTL ? 1 : 0) | \
-                      (TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::B_DTL ? 2 : 0) | \
-                      (TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::A_TR ? 4 : 0) |  \
-                      (TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL>::B_TR ? 8 : 0)}, \
-          &launch_tile<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, PP, DTL>}
+                      TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL, MI>::BK, (WM) * (WN), 1, PERM, \
+                      TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL, MI>::lds_alloc(PP),  \
+                      TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL, MI>::NSETS, 1, PP,   \
+                      (TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL, MI>::A_DTL ? 1 : 0) | \
+                      (TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL, MI>::B_DTL ? 2 : 0) | \
+                      (TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL, MI>::A_TR ? 4 : 0) |  \
+                      (TileCfg<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, DTL, MI>::B_TR ? 8 : 0), MI}, \
+          &launch_tile<T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, PP, DTL, MI>}
+#define TILE_X(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, PP, DTL) TILE_XM(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, PP, DTL, 32)
 #define TILE_PP(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, PP) TILE_X(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, PP, 0)
 #define TILE(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM) TILE_X(T, AKC, BKC, U4, MTM, MTN, WM, WN, PERM, false, 0)
 #define TILE_DTL(T, AKC, BKC, U4, MTM, MTN, WM, WN) TILE_X(T, AKC, BKC, U4, MTM, MTN, WM, WN, true, false, 1)
@@ -1753,13 +1894,22 @@ struct Variant {
   TILE_X(T, false, true, false, MTM, MTN, WM, WN, true, true, 2),                          \
   TILE_X(T, false, false, false, MTM, MTN, WM, WN, true, true, 2)
 
-// Every layout on schedule 2 (4 waves of 128x128, every operand straight into LDS, the
-// transposed ones transposed by the LDS reads, one barrier per step after sub-step 2).
-#define TILE_LAYOUTS_W4(T)                                                                   \
-  TILE_X(T, true, true, false, 256, 256, 2, 2, true, 2, 1),                                \
-  TILE_X(T, false, true, false, 256, 256, 2, 2, true, 2, 2),                               \
-  TILE_X(T, true, false, false, 256, 256, 2, 2, true, 2, 2),                               \
-  TILE_X(T, false, false, false, 256, 256, 2, 2, true, 2, 2)
+// Every layout on schedule 2 (4 waves, every operand straight into LDS, the transposed
+// ones transposed by the LDS reads, one barrier per step after sub-step 2).
+#define TILE_LAYOUTS_W4(T, MTM, MTN)                                                         \
+  TILE_X(T, true, true, false, MTM, MTN, 2, 2, true, 2, 1),                                \
+  TILE_X(T, false, true, false, MTM, MTN, 2, 2, true, 2, 2),                               \
+  TILE_X(T, true, false, false, MTM, MTN, 2, 2, true, 2, 2),                               \
+  TILE_X(T, false, false, false, MTM, MTN, 2, 2, true, 2, 2)
+
+// Every layout on the ping-pong schedule with 16x16x32 blocks and every operand straight
+// into LDS (K-contiguous ones in rows, transposed ones in 64-wide K-row segments for the
+// transposing reads): 8-wave tiles whose wave tiles are not whole 32x32 blocks.
+#define TILE_LAYOUTS_PP16(T, MTM, MTN)                                                       \
+  TILE_XM(T, true, true, false, MTM, MTN, 2, 4, true, 1, 1, 16),                           \
+  TILE_XM(T, false, true, false, MTM, MTN, 2, 4, true, 1, 2, 16),                          \
+  TILE_XM(T, true, false, false, MTM, MTN, 2, 4, true, 1, 2, 16),                          \
+  TILE_XM(T, false, false, false, MTM, MTN, 2, 4, true, 1, 2, 16)
 
 #define TILE_LAYOUTS_PP(T, MTM, MTN, WM, WN)                                                 \
   TILE_PP(T, true, true, false, MTM, MTN, WM, WN, true, true),                             \
@@ -1769,7 +1919,7 @@ struct Variant {
 
 #define SKINNY(T, U4, NB, W, U, SLOTS)                                                       \
   Variant{VariantInfo{KERNEL_SKINNY, dt_code<T>(), (U4) ? DT_U4 : dt_code<T>(), 0, 1, 16,     \
-                      16 * (NB), (U4) ? 128 : 64, W, W, 0, 0, U, SLOTS, 0, 0},               \
+                      16 * (NB), (U4) ? 128 : 64, W, W, 0, 0, U, SLOTS, 0, 0, 16},           \
           &launch_skinny<T, U4, NB, W, U>}
 
 

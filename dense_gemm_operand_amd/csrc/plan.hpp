@@ -65,6 +65,7 @@ struct VariantInfo {
   int32_t sched;                  // tiled: 0 = software pipeline, 1 = ping-pong wave groups
   int32_t dtl;                    // tiled: bit 0 A, bit 1 B loaded straight into LDS;
                                   // bit 2 A, bit 3 B transposed by the LDS reads
+  int32_t mfma;                   // matrix-core block: 32 (32x32x16 / 32x32x64) or 16 (16x16x32)
 };
 
 // One attention forward call (validated by the ABI layer).

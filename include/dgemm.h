@@ -100,12 +100,21 @@ typedef struct {
                               padding, 16-byte chunks permuted by an XOR of the row);
                               lds_pad_bytes then applies to the other operand only.
                               bit 2 (A), bit 3 (B): the transposed operand is also loaded
-                              straight into LDS in global order (1 KiB blocks of two K rows
-                              plus lds_pad_bytes = 64, K rows permuted with perm_block = 8,
-                              perm_stride = 4) and transposed by the LDS reads */
+                              straight into LDS in global order (1 KiB blocks plus
+                              lds_pad_bytes = 64) and transposed by the LDS reads; on
+                              256-wide tiles a block holds two K rows, K rows permuted with
+                              perm_block = 8, perm_stride = 4; on other widths (192, 320) a
+                              block holds eight 64-wide K-row segments, K rows permuted with
+                              perm_block = 64, perm_stride = 8 */
   int32_t schedule;        /* tiled kernel's main loop: 0 = one software pipeline for all
                               waves, 1 = two wave groups in ping-pong (one multiplies while
-                              the other reads LDS); 0 for the skinny kernel */
+                              the other reads LDS), 2 = four waves with every operand loaded
+                              straight into LDS and one barrier per step (no split-K); 0 for
+                              the skinny kernel */
+  int32_t mfma_m;          /* rows (= columns) of the matrix-core instruction's output block:
+                              32 (v_mfma_f32_32x32x16, fp8 v_mfma_f32_32x32x64) or 16
+                              (v_mfma_f32_16x16x32: the skinny kernel, and 8-wave tiles whose
+                              per-wave share is not whole 32x32 blocks, e.g. 96x80 of 192x320) */
 } gemm_plan_info_t;
 
 /* Make a plan for C (M x N, row-major, dtype_c) = A (M x K) * B (K x N).

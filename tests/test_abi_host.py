@@ -173,33 +173,47 @@ def test_headline_plans(fake_cus):
     assert i["direct_lds"] == 2   # B (column-major, K-contiguous) goes straight to LDS
     assert i["schedule"] == 1     # two wave groups in ping-pong
     assert i["lds_bytes"] <= 160 * 1024
-    # 3072x5120: the 8-wave 256x256 kernel (240 tiles) is charged less than the 4-wave
-    # 192x320 one (256 tiles); at 2880x5440 (264 tiles of 256x256, two rounds on 256 CUs,
-    # against 255 of 192x320) the non-power-of-2 tile wins
-    p = dg.gemm_plan(3072, 5120, 6144, COL, ROW, BF16, BF16, BF16, 0)
-    i = dg.gemm_plan_query(p)
+    # 3072x5120: the non-power-of-2 192x320 tile (16 x 16 = 256 tiles, one per CU) on the
+    # 8-wave ping-pong with 16x16x32 blocks, against 240 tiles of 256x256; both transposed
+    # operands straight into LDS in 64-wide K-row segments (B = 64, S = 8, 64 B pad). The
+    # same at 2880x5440 (255 tiles against 264 of 256x256, two rounds on 256 CUs), where the
+    # split-K search, counting the one empty slot as waste, doubles up to its cap of 16.
+    for M, N, grid, sk in ((3072, 5120, 256, 1), (2880, 5440, 255, 16)):
+        p = dg.gemm_plan(M, N, 6144, COL, ROW, BF16, BF16, BF16, 0)
+        i = dg.gemm_plan_query(p)
+        dg.gemm_plan_destroy(p)
+        assert (i["tile_m"], i["tile_n"], i["grid_x"], i["waves"]) == (192, 320, grid, 8)
+        assert (i["schedule"], i["mfma_m"], i["direct_lds"], i["split_k"]) == (1, 16, 12, sk)
+        assert (i["perm_block"], i["perm_stride"], i["lds_pad_bytes"]) == (64, 8, 64)
+    # the 4096^3 headline stays on 256x256 tiles with 32x32x16 blocks
+    p = dg.gemm_plan(4096, 4096, 4096, COL, COL, F16, F16, F16, 0)
+    assert dg.gemm_plan_query(p)["mfma_m"] == 32
     dg.gemm_plan_destroy(p)
-    assert (i["tile_m"], i["tile_n"], i["grid_x"], i["waves"]) == (256, 256, 240, 8)
-    p = dg.gemm_plan(2880, 5440, 6144, COL, ROW, BF16, BF16, BF16, 0)
-    i = dg.gemm_plan_query(p)
-    dg.gemm_plan_destroy(p)
-    assert (i["tile_m"], i["tile_n"], i["grid_x"]) == (192, 320, 255)   # non-power-of-2 tile
 
 
 @pytest.mark.parametrize("dt", [F16, BF16])
 @pytest.mark.parametrize("M,N,K", [(4096, 4096, 4096), (3072, 5120, 6144), (8192, 8192, 520)])
 def test_default_loader_and_schedule_per_layout(fake_cus, dt, M, N, K):
-    # every layout runs the ping-pong schedule on 256x256 tiles; K-contiguous operands go
-    # straight into LDS; a transposed operand is transposed in registers (64-row stride-8
-    # permuted rows) unless both are transposed (NT), where both go straight into LDS in
-    # global order and the LDS reads transpose them (blocks of 8 K rows, stride 4, 64 B pad)
-    want = {(ROW, COL): (3, (1, 1), 0), (COL, COL): (2, (64, 8), 16), (ROW, ROW): (1, (64, 8), 16),
-            (COL, ROW): (12, (8, 4), 64)}
+    # every layout runs the 8-wave ping-pong schedule. On 256x256 tiles K-contiguous
+    # operands go straight into LDS; a transposed operand is transposed in registers (64-row
+    # stride-8 permuted rows) unless both are transposed (NT), where both go straight into
+    # LDS in global order and the LDS reads transpose them (blocks of 8 K rows, stride 4,
+    # 64 B pad). At 3072x5120 the 192x320 tile (16x16x32 blocks) takes every operand straight
+    # into LDS, transposed ones in 64-wide K-row segments (B = 64, S = 8, 64 B pad).
+    if (M, N) == (3072, 5120):
+        tile, mfma = (192, 320), 16
+        want = {(ROW, COL): (3, (1, 1), 0), (COL, COL): (6, (64, 8), 64),
+                (ROW, ROW): (9, (64, 8), 64), (COL, ROW): (12, (64, 8), 64)}
+    else:
+        tile, mfma = (256, 256), 32
+        want = {(ROW, COL): (3, (1, 1), 0), (COL, COL): (2, (64, 8), 16),
+                (ROW, ROW): (1, (64, 8), 16), (COL, ROW): (12, (8, 4), 64)}
     for (la, lb), (bits, perm, pad) in want.items():
         p = dg.gemm_plan(M, N, K, la, lb, dt, dt, dt, 1)
         i = dg.gemm_plan_query(p)
         dg.gemm_plan_destroy(p)
-        assert (i["tile_m"], i["tile_n"], i["waves"], i["schedule"]) == (256, 256, 8, 1), (la, lb)
+        assert (i["tile_m"], i["tile_n"], i["waves"], i["schedule"]) == (*tile, 8, 1), (la, lb)
+        assert i["mfma_m"] == mfma, (la, lb)
         assert i["direct_lds"] == bits, (la, lb)
         assert (i["perm_block"], i["perm_stride"]) == perm, (la, lb)
         assert i["lds_pad_bytes"] == pad, (la, lb)

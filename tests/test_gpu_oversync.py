@@ -47,13 +47,14 @@ def _inputs(M, N, K, la, lb, fmt, seed):
             "A": synth.store(a, la), "B": synth.store(b, lb)}
 
 
-def _both(inp, fmt, out, hooks, split_k=1):
-    with env(DGEMM_FORCE_TILE="256x256", **hooks):
-        ref, info = run_gpu(inp, fmt, out, split_k=split_k, guard=8)
+def _both(inp, fmt, out, hooks, split_k=1, tile="256x256"):
+    with env(**hooks):
+        ref, info = run_gpu(inp, fmt, out, split_k=split_k, guard=8, force_tile=tile)
         with library(dg_build.LIB_OVERSYNC):
-            got, info2 = run_gpu(inp, fmt, out, split_k=split_k, guard=8)
-    assert {k: info[k] for k in ("tile_m", "waves", "schedule", "direct_lds", "split_k")} == \
-        {k: info2[k] for k in ("tile_m", "waves", "schedule", "direct_lds", "split_k")}
+            got, info2 = run_gpu(inp, fmt, out, split_k=split_k, guard=8, force_tile=tile)
+    keys = ("tile_m", "tile_n", "waves", "schedule", "direct_lds", "split_k")
+    assert {k: info[k] for k in keys} == {k: info2[k] for k in keys}
+    assert f"{info['tile_m']}x{info['tile_n']}" == tile
     return ref, got, info
 
 
@@ -63,10 +64,11 @@ LAYOUTS = [("col", "col"), ("col", "row"), ("row", "col"), ("row", "row")]
 SCHED_LOADER = [(1, 1), (1, 2), (1, 0), (0, 0), (0, 1), (0, 2), (2, 1), (2, 2)]
 
 
-def _served(sched, loader, la, lb):
+def _served(sched, loader, la, lb, tile="256x256"):
     transposed = la == "col" or lb == "row"
     kcontig = la == "row" or lb == "col"
-    if sched == 2:   # every operand direct: loader 1 for TN, loader 2 wherever one is transposed
+    if sched == 2 or tile == "192x320" and sched == 1:
+        # every operand direct: loader 1 for TN, loader 2 wherever one is transposed
         return transposed if loader == 2 else (loader == 1 and not transposed)
     return {0: True, 1: kcontig, 2: transposed}[loader]
 
@@ -81,6 +83,22 @@ def test_oversynchronised_build_bit_identical(sched, loader, la, lb):
     inp = _inputs(M, N, K, la, lb, "f16", seed=301 + 7 * sched + loader)
     ref, got, info = _both(inp, "f16", "f32", {"DGEMM_FORCE_SCHED": sched, "DGEMM_FORCE_DTL": loader})
     assert info["schedule"] == sched
+    assert np.array_equal(ref, got), f"{int((ref != got).sum())} of {ref.size} elements differ"
+
+
+@pytest.mark.parametrize("sched,loader", [(1, 2), (1, 1), (0, 2), (2, 2), (2, 1)])
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_oversynchronised_build_bit_identical_nonpow2_tile(sched, loader, la, lb):
+    # the 192 x 320 tile with direct-to-LDS loads (64-wide K-row segments for transposed
+    # operands): 2 x 3 tiles with ragged edges, 10 K steps and a tail
+    if not _served(sched, loader, la, lb, "192x320"):
+        pytest.skip("this loader serves no operand of this layout pair")
+    M, N, K = 392, 720, 680
+    _say("oversync 192x320", sched, loader, la, lb)
+    inp = _inputs(M, N, K, la, lb, "bf16", seed=341 + 7 * sched + loader)
+    ref, got, info = _both(inp, "bf16", "f32", {"DGEMM_FORCE_SCHED": sched, "DGEMM_FORCE_DTL": loader},
+                           tile="192x320")
+    assert (info["tile_m"], info["schedule"]) == (192, sched)
     assert np.array_equal(ref, got), f"{int((ref != got).sum())} of {ref.size} elements differ"
 
 

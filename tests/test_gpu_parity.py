@@ -281,6 +281,84 @@ def test_every_schedule_variant_bit_exact(sched, dtl, waves, la, lb):
     assert np.array_equal(c, ref)
 
 
+# The non-power-of-2 192x320 tile: (schedule, loader). Loader 0 = register-staged loads;
+# 1 = K-contiguous operands straight into LDS; 2 = transposed operands too, in 64-wide K-row
+# segments, transposed by the LDS reads. Schedule 1 is the 8-wave ping-pong with 16x16x32
+# blocks (96x80 per wave), schedules 0 and 2 use 4 waves of 96x160 in 32x32x16 blocks.
+NONPOW2 = [(1, 1), (1, 2), (0, 0), (0, 1), (0, 2), (2, 1), (2, 2)]
+
+
+def _nonpow2_served(sched, dtl, la, lb):
+    if dtl == 0:
+        return True    # register-staged loads serve every layout
+    if dtl == 1 and (la, lb) == ("col", "row"):
+        return False   # no K-contiguous operand
+    if dtl == 2 and (la, lb) == ("row", "col"):
+        return False   # no transposed operand
+    # schedules 1 and 2 load every operand straight into LDS: loader 1 serves TN only
+    return not (sched in (1, 2) and dtl == 1 and (la, lb) != ("row", "col"))
+
+
+def _nonpow2_bits(dtl, la, lb):
+    if dtl == 0:
+        return 0
+    a_kc, b_kc = la == "row", lb == "col"
+    bits = (1 if a_kc else 0) | (2 if b_kc else 0)
+    if dtl == 2:
+        bits |= (0 if a_kc else 4) | (0 if b_kc else 8)
+    return bits
+
+
+@pytest.mark.parametrize("sched,dtl", NONPOW2)
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_nonpow2_tile_direct_to_lds_bit_exact(sched, dtl, la, lb, fmt):
+    # 192x320 tiles: two whole tiles and a ragged one in M (392 = 2 x 192 + 8) and in N
+    # (648 = 2 x 320 + 8), 7 K steps and a ragged tail (456 = 7 x 64 + 8)
+    if not _nonpow2_served(sched, dtl, la, lb):
+        pytest.skip("this loader serves no operand of this layout pair on this schedule")
+    from helpers import env
+    M, N, K = 392, 648, 456
+    _say("nonpow2", sched, dtl, la, lb, fmt)
+    inp = _inputs_int(M, N, K, la, lb, fmt, seed=151 + dtl)
+    with env(DGEMM_FORCE_SCHED=sched, DGEMM_FORCE_DTL=dtl):
+        c, info = run_gpu(inp, fmt, "f32", split_k=1, force_tile="192x320", guard=64)
+    assert (info["tile_m"], info["tile_n"], info["schedule"]) == (192, 320, sched)
+    assert (info["waves"], info["mfma_m"]) == ((8, 16) if sched == 1 else (4, 32))
+    assert info["direct_lds"] == _nonpow2_bits(dtl, la, lb)
+    if dtl == 2:
+        assert (info["perm_block"], info["perm_stride"], info["lds_pad_bytes"]) == (64, 8, 64)
+    _, ref = reference(inp, fmt, "f32")
+    assert np.array_equal(c, ref)
+
+
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_nonpow2_tile_direct_to_lds_split_k_and_random(la, lb):
+    # the pipeline schedule with split-K (the partial tiles of 192 x 320 through the
+    # fix-up), and random bf16 inputs to the acceptance bar on both schedules
+    from helpers import env
+    dtl = 1 if (la, lb) == ("row", "col") else 2
+    M, N, K = 200, 328, 1032
+    _say("nonpow2 split", la, lb, dtl)
+    inp = _inputs_int(M, N, K, la, lb, "f16", seed=157)
+    _, ref = reference(inp, "f16", "f32")
+    for sched in (1, 0):
+        with env(DGEMM_FORCE_SCHED=sched, DGEMM_FORCE_DTL=dtl):
+            for sk in (1, 4):
+                c, info = run_gpu(inp, "f16", "f32", split_k=sk, force_tile="192x320", guard=16)
+                assert info["split_k"] == sk and info["direct_lds"] == _nonpow2_bits(dtl, la, lb)
+                assert info["schedule"] == sched
+                assert np.array_equal(c, ref), (sched, sk)
+    inp = _inputs_rand(520, 392, 328, la, lb, "bf16", seed=159)
+    _, ref = reference(inp, "bf16", "bf16")
+    amax, bmax = operand_max(inp, "bf16")
+    for sched in (1, 0, 2):
+        with env(DGEMM_FORCE_SCHED=sched, DGEMM_FORCE_DTL=dtl):
+            c, info = run_gpu(inp, "bf16", "bf16", split_k=1, force_tile="192x320", guard=16)
+        assert info["schedule"] == sched
+        check_tolerance(c, ref, "bf16", 328, amax, bmax, f"nonpow2 sched {sched}")
+
+
 def _int4_group_inputs(M, N, K, group, seed):
     # codes U{0..15} packed along K, scales [K/group][N]; A = unit rows, so C rows are
     # dequantised weight rows exactly
