@@ -294,8 +294,10 @@ def loader_comparison(rounds: int = 5, calls: int = 20) -> list:
     """The two loaders for transposed operands on the same shapes, timed interleaved: the
     in-register transpose (the default where one operand is K-contiguous; planner hook
     DGEMM_FORCE_DTL=0 where none is) and direct-to-LDS loads in global order transposed by
-    the LDS reads (DGEMM_FORCE_DTL=2; the default for NT). The default kernel's own time is
-    the one under "workloads"; here only the alternative's time and the ratio appear."""
+    the LDS reads (the default for NT; where one operand is K-contiguous, the fastest such
+    kernel, 16x16x32 blocks: DGEMM_FORCE_DTL=2 DGEMM_FORCE_MFMA=16). The default kernel's own
+    time is the one under "workloads"; here only the alternative's time and the ratio
+    appear."""
     import torch
     from dense_gemm_operand_amd import synth
     res = []
@@ -304,19 +306,20 @@ def loader_comparison(rounds: int = 5, calls: int = 20) -> list:
         wl = synth.WORKLOADS[name]
         nt = (la or wl.layout_a) == "col" and (lb or wl.layout_b) == "row"
         hs = []
-        for dtl in (None, "2" if not nt else "0"):   # default first, then the other loader
-            if dtl is not None:
-                os.environ["DGEMM_FORCE_DTL"] = dtl
+        alt_env = {"DGEMM_FORCE_DTL": "0"} if nt else {"DGEMM_FORCE_DTL": "2", "DGEMM_FORCE_MFMA": "16"}
+        for envs in ({}, alt_env):   # default first, then the other loader
+            os.environ.update(envs)
             try:
                 hs.append(Gemm(wl, la, lb))
             finally:
-                os.environ.pop("DGEMM_FORCE_DTL", None)
+                for k in envs:
+                    os.environ.pop(k, None)
         d, alt = interleaved([hs[0].run, hs[1].run], rounds, calls)
         loader = lambda h: "transposing_lds_reads" if h.info["direct_lds"] & 12 else "in_register_transpose"
-        tile = lambda h: f"{h.info['tile_m']}x{h.info['tile_n']}"
+        kern = lambda h: f"{h.info['tile_m']}x{h.info['tile_n']}, {h.info['mfma_m']}x{h.info['mfma_m']} blocks"
         rec = {"workload": name, "layout_a": hs[0].la, "layout_b": hs[0].lb,
                "default": loader(hs[0]), "alternative": loader(hs[1]),
-               "default_tile": tile(hs[0]), "alternative_tile": tile(hs[1]),
+               "default_kernel": kern(hs[0]), "alternative_kernel": kern(hs[1]),
                "alternative_us": round(alt * 1e3, 2),
                "alternative_over_default": round(alt / d, 4)}
         log(json.dumps(rec))

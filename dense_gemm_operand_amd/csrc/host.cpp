@@ -179,9 +179,10 @@ int make_plan(Plan& p, int split_k_req) {
     // K-row permutation B = 8, S = 4 (256-wide tiles, two K rows per block) or B = 64,
     // S = 8 (other widths, eight 64-wide K-row segments per block)
     const int tr_rows = (p.direct_lds & 4) ? p.tile_m : p.tile_n;
+    const bool two_rows = tr_rows == 256 && v.mfma == 32;
     p.lds_pad = 64;
-    p.perm_block = tr_rows == 256 ? 8 : 64;
-    p.perm_stride = tr_rows == 256 ? 4 : 8;
+    p.perm_block = two_rows ? 8 : 64;
+    p.perm_stride = two_rows ? 4 : 8;
   }
   if (v.kernel == KERNEL_SKINNY) {
     p.lds_pad = 0;

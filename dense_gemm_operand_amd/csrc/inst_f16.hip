@@ -4,12 +4,17 @@
 namespace dg {
 
 static const Variant kTable[] = {
-    // Defaults first (the planner takes the first match): the ping-pong schedule, with
-    // direct-to-LDS loads for the K-contiguous operands (TN, TT, NN: the transposed operand
-    // goes through the in-register transpose); for NT, where both operands are transposed,
-    // both go straight into LDS and are transposed by the LDS reads (the in-register
-    // transpose of both measured 11-18% slower; DGEMM_FORCE_DTL=0 selects it). The
-    // single-schedule pipeline kernels follow (DGEMM_FORCE_SCHED=0).
+    // Defaults first (the planner takes the first match), all on the 8-wave ping-pong
+    // schedule: TN (both operands K-contiguous) and NT (both transposed) with 16x16x32
+    // blocks and every operand straight into LDS (NT's in 64-wide K-row segments,
+    // transposed by the LDS reads); NN and TT with 32x32x16 blocks, the K-contiguous
+    // operand straight into LDS and the transposed one through the in-register
+    // transpose. Then the alternatives: 32x32x16 blocks for TN and NT (NT transposed by
+    // the LDS reads; the in-register transpose of both measured 11-18% slower,
+    // DGEMM_FORCE_DTL=0), the single-schedule pipeline kernels (DGEMM_FORCE_SCHED=0), and
+    // NN and TT with 16x16x32 blocks and transposing reads (DGEMM_FORCE_MFMA=16).
+    TILE_XM(F16T, true, true, false, 256, 256, 2, 4, true, 1, 1, 16),
+    TILE_XM(F16T, false, false, false, 256, 256, 2, 4, true, 1, 2, 16),
     TILE_LAYOUTS_PPDTL(F16T, 256, 256, 2, 4),
     TILE_LAYOUTS_PPTR(F16T, 256, 256, 2, 4),
     TILE_LAYOUTS_PP(F16T, 256, 256, 2, 4),
@@ -30,6 +35,8 @@ static const Variant kTable[] = {
     TILE_LAYOUTS_DTL(F16T, 256, 256, 2, 2),
     TILE_LAYOUTS_DTLTR(F16T, 256, 256, 2, 4),
     TILE_LAYOUTS_W4(F16T, 256, 256),
+    TILE_XM(F16T, false, true, false, 256, 256, 2, 4, true, 1, 2, 16),
+    TILE_XM(F16T, true, false, false, 256, 256, 2, 4, true, 1, 2, 16),
 };
 
 int variants_f16(const Variant** out) {

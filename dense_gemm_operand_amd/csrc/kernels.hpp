@@ -512,10 +512,10 @@ struct DtlOperand {
 //    16-lane groups of a half-wave on rows i and i + 1 of the same four blocks, 128 B
 //    apart) the swap moves the odd row's 32 bytes to the other half of the same 64-byte
 //    bank group, so both shapes read free of bank conflicts.
-template <int ROWS, int THREADS>
+template <int ROWS, int THREADS, bool SEG_ = ROWS != 256>
 struct DtlTrOperand {
   static_assert(ROWS % 64 == 0, "whole 64-wide segments");
-  static constexpr bool SEG = ROWS != 256;
+  static constexpr bool SEG = SEG_;
   static constexpr int WAVES = THREADS / 64;
   static constexpr int BLOCKS = ROWS / 8;         // 64 K rows x ROWS x 2 B per step, 1 KiB each
   static constexpr int NI = BLOCKS / WAVES;       // load instructions per wave and K step
@@ -641,8 +641,9 @@ struct TileCfg {
   using OpB = Operand<U4B ? 2 : (B_KC ? 0 : KT), MT_N, THREADS, PB, EB, PITCH>;
   using DA = DtlOperand<MT_M, THREADS, EB>;
   using DB = DtlOperand<MT_N, THREADS, EB>;
-  using TA = DtlTrOperand<A_TR ? MT_M : 256, THREADS>;
-  using TB = DtlTrOperand<B_TR ? MT_N : 256, THREADS>;
+  // (the 16x16x32 kernels read transposed operands from the segment layout at any width)
+  using TA = DtlTrOperand<A_TR ? MT_M : 256, THREADS, (A_TR ? MT_M : 256) != 256 || MI == 16>;
+  using TB = DtlTrOperand<B_TR ? MT_N : 256, THREADS, (B_TR ? MT_N : 256) != 256 || MI == 16>;
   // Register-staged load slots per thread (none for a direct-to-LDS operand).
   static constexpr int SA = (A_DTL || A_TR) ? 0 : OpA::SLOTS;
   static constexpr int SB = (B_DTL || B_TR) ? 0 : OpB::SLOTS;
@@ -660,10 +661,10 @@ struct TileCfg {
   static constexpr int NSETS = (SA + SB) > 4 ? 1 : 2;
   static_assert(!ANY_DTL || NSETS == 2, "direct-to-LDS schedule keeps loads a step ahead");
   static_assert(WT_M % MI == 0 && WT_N % MI == 0, "wave tile must be whole MIxMI blocks");
-  // 16x16x32 blocks: 16-bit operands, every operand straight into LDS (the direct epilogue
-  // assumes LDS rows in logical order)
-  static_assert(MI == 32 || (!F8 && !U4B && SA == 0 && SB == 0 && PA.block == 1 && PB.block == 1),
-                "16x16x32 blocks: 16-bit operands loaded straight into LDS");
+  // 16x16x32 blocks: 16-bit operands; B's LDS rows in logical order (the direct epilogue
+  // stores four consecutive columns per lane; A's permuted rows it maps back one per lane)
+  static_assert(MI == 32 || (!F8 && !U4B && SB == 0 && PB.block == 1),
+                "16x16x32 blocks: 16-bit operands, B straight into LDS");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -1526,8 +1527,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   // cover 16 contiguous bytes of 32 rows (fp16), and the 16 stores of a block fill whole
   // 128-byte lines of those rows. No LDS round trip, and no accumulator needs to wait for a
   // second pass (the two-pass LDS epilogue of an fp32 tile would not fit the registers).
-  // The 16x16x32 kernels do the same: lane l of block (i, j) holds row 16i + l%16 and the
-  // four consecutive columns 16j + 4(l/16) + 0..3 (operands in logical order in LDS).
+  // The 16x16x32 kernels do the same: lane l of block (i, j) holds A's LDS row 16i + l%16
+  // (logical row fwd_A of it) and the four consecutive columns 16j + 4(l/16) + 0..3.
   auto epilogue_direct = [&](auto dt_tag) {
     constexpr int DT = decltype(dt_tag)::value;
     using O = typename OutT<DT>::type;
@@ -1536,7 +1537,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
     if constexpr (MI == 16) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const int gm = m0 + wm * Cfg::WT_M + i * 16 + r16;
+        const int gm = m0 + PA.fwd(wm * Cfg::WT_M + i * 16 + r16);   // logical row of A
         if (gm >= a.M) continue;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {

@@ -185,7 +185,7 @@ def test_headline_plans(fake_cus):
         assert (i["tile_m"], i["tile_n"], i["grid_x"], i["waves"]) == (192, 320, grid, 8)
         assert (i["schedule"], i["mfma_m"], i["direct_lds"], i["split_k"]) == (1, 16, 12, sk)
         assert (i["perm_block"], i["perm_stride"], i["lds_pad_bytes"]) == (64, 8, 64)
-    # the 4096^3 headline stays on 256x256 tiles with 32x32x16 blocks
+    # the 4096^3 headline (NN, in-register transpose of A) stays on 32x32x16 blocks
     p = dg.gemm_plan(4096, 4096, 4096, COL, COL, F16, F16, F16, 0)
     assert dg.gemm_plan_query(p)["mfma_m"] == 32
     dg.gemm_plan_destroy(p)
@@ -197,23 +197,25 @@ def test_default_loader_and_schedule_per_layout(fake_cus, dt, M, N, K):
     # every layout runs the 8-wave ping-pong schedule. On 256x256 tiles K-contiguous
     # operands go straight into LDS; a transposed operand is transposed in registers (64-row
     # stride-8 permuted rows) unless both are transposed (NT), where both go straight into
-    # LDS in global order and the LDS reads transpose them (blocks of 8 K rows, stride 4,
-    # 64 B pad). At 3072x5120 the 192x320 tile (16x16x32 blocks) takes every operand straight
-    # into LDS, transposed ones in 64-wide K-row segments (B = 64, S = 8, 64 B pad).
+    # LDS in global order, in 64-wide K-row segments (B = 64, S = 8, 64 B pad), and the LDS
+    # reads transpose them. At 3072x5120 the 192x320 tile (16x16x32 blocks) takes every
+    # operand straight into LDS, transposed ones in the same segments.
     if (M, N) == (3072, 5120):
         tile, mfma = (192, 320), 16
         want = {(ROW, COL): (3, (1, 1), 0), (COL, COL): (6, (64, 8), 64),
                 (ROW, ROW): (9, (64, 8), 64), (COL, ROW): (12, (64, 8), 64)}
     else:
-        tile, mfma = (256, 256), 32
+        # TN and NT (no operand for the in-register transpose) in 16x16x32 blocks, NT's
+        # transposed operands in 64-wide K-row segments; NN and TT in 32x32x16 blocks
+        tile, mfma = (256, 256), {(ROW, COL): 16, (COL, ROW): 16, (COL, COL): 32, (ROW, ROW): 32}
         want = {(ROW, COL): (3, (1, 1), 0), (COL, COL): (2, (64, 8), 16),
-                (ROW, ROW): (1, (64, 8), 16), (COL, ROW): (12, (8, 4), 64)}
+                (ROW, ROW): (1, (64, 8), 16), (COL, ROW): (12, (64, 8), 64)}
     for (la, lb), (bits, perm, pad) in want.items():
         p = dg.gemm_plan(M, N, K, la, lb, dt, dt, dt, 1)
         i = dg.gemm_plan_query(p)
         dg.gemm_plan_destroy(p)
         assert (i["tile_m"], i["tile_n"], i["waves"], i["schedule"]) == (*tile, 8, 1), (la, lb)
-        assert i["mfma_m"] == mfma, (la, lb)
+        assert i["mfma_m"] == (mfma if isinstance(mfma, int) else mfma[(la, lb)]), (la, lb)
         assert i["direct_lds"] == bits, (la, lb)
         assert (i["perm_block"], i["perm_stride"]) == perm, (la, lb)
         assert i["lds_pad_bytes"] == pad, (la, lb)

@@ -62,6 +62,8 @@ LAYOUTS = [("col", "col"), ("col", "row"), ("row", "col"), ("row", "row")]
 # (schedule, loader): loader 0 = transposed operands through registers, 1 = K-contiguous
 # operands straight into LDS, 2 = transposed operands straight into LDS, transposed by the reads
 SCHED_LOADER = [(1, 1), (1, 2), (1, 0), (0, 0), (0, 1), (0, 2), (2, 1), (2, 2)]
+# the 16x16x32 ping-pong (every operand direct) at 256x256
+SCHED_LOADER16 = [(1, 1), (1, 2)]
 
 
 def _served(sched, loader, la, lb, tile="256x256"):
@@ -73,16 +75,19 @@ def _served(sched, loader, la, lb, tile="256x256"):
     return {0: True, 1: kcontig, 2: transposed}[loader]
 
 
-@pytest.mark.parametrize("sched,loader", SCHED_LOADER)
+@pytest.mark.parametrize("sched,loader,mfma", [(s, l, 32) for s, l in SCHED_LOADER] +
+                         [(s, l, 16) for s, l in SCHED_LOADER16])
 @pytest.mark.parametrize("la,lb", LAYOUTS)
-def test_oversynchronised_build_bit_identical(sched, loader, la, lb):
-    if not _served(sched, loader, la, lb):
+def test_oversynchronised_build_bit_identical(sched, loader, mfma, la, lb):
+    # (the 16x16x32 ping-pong loads every operand directly, as schedule 2 does)
+    if not _served(2 if mfma == 16 else sched, loader, la, lb):
         pytest.skip("this loader serves no operand of this layout pair")
     M, N, K = 520, 264, 712   # 3 x 2 tiles of 256 x 256, ragged edges, 11 K steps + a tail
-    _say("oversync", sched, loader, la, lb)
+    _say("oversync", sched, loader, mfma, la, lb)
     inp = _inputs(M, N, K, la, lb, "f16", seed=301 + 7 * sched + loader)
-    ref, got, info = _both(inp, "f16", "f32", {"DGEMM_FORCE_SCHED": sched, "DGEMM_FORCE_DTL": loader})
-    assert info["schedule"] == sched
+    ref, got, info = _both(inp, "f16", "f32", {"DGEMM_FORCE_SCHED": sched, "DGEMM_FORCE_DTL": loader,
+                                               "DGEMM_FORCE_MFMA": mfma})
+    assert info["schedule"] == sched and info["mfma_m"] == mfma
     assert np.array_equal(ref, got), f"{int((ref != got).sum())} of {ref.size} elements differ"
 
 

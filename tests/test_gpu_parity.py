@@ -218,20 +218,23 @@ def _dtl_bits(la, lb):
     return (1 if la == "row" else 0) | (2 if lb == "col" else 0)
 
 
-@pytest.mark.parametrize("waves,sched", [(8, 1), (8, 0), (4, 0)])
+@pytest.mark.parametrize("waves,sched,mfma", [(8, 1, 32), (8, 1, 16), (8, 0, 32), (4, 0, 32)])
 @pytest.mark.parametrize("la,lb", DTL_LAYOUTS)
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
-def test_direct_to_lds_integer_bit_exact(waves, sched, la, lb, fmt):
+def test_direct_to_lds_integer_bit_exact(waves, sched, mfma, la, lb, fmt):
     # K-contiguous operands loaded straight into swizzled LDS rows, in the ping-pong (1) and
-    # the pipeline (0) schedule; ragged M, N and K (K = 200: the last step has one 8-wide
-    # chunk) exercise the out-of-range zero fill
+    # the pipeline (0) schedule, in 32x32x16 and (ping-pong, TN) 16x16x32 blocks; ragged M,
+    # N and K (K = 200: the last step has one 8-wide chunk) exercise the out-of-range zero fill
+    if mfma == 16 and (la, lb) != ("row", "col"):
+        pytest.skip("16x16x32 blocks with loader 1: TN only")
     M, N, K = 392 + 8, 648, 200
-    _say("dtl-int", waves, sched, la, lb, fmt)
+    _say("dtl-int", waves, sched, mfma, la, lb, fmt)
     inp = _inputs_int(M, N, K, la, lb, fmt, seed=91)
     from helpers import env
-    with env(DGEMM_FORCE_DTL=1, DGEMM_FORCE_WAVES=waves, DGEMM_FORCE_SCHED=sched):
+    with env(DGEMM_FORCE_DTL=1, DGEMM_FORCE_WAVES=waves, DGEMM_FORCE_SCHED=sched, DGEMM_FORCE_MFMA=mfma):
         c, info = run_gpu(inp, fmt, "f32", split_k=1, force_tile="256x256", guard=64)
     assert info["direct_lds"] == _dtl_bits(la, lb) and info["waves"] == waves
+    assert info["mfma_m"] == mfma
     _, ref = reference(inp, fmt, "f32")
     assert np.array_equal(c, ref)
 
@@ -255,27 +258,29 @@ def test_direct_to_lds_split_k_and_random(la, lb):
     check_tolerance(c, ref, "bf16", 328, amax, bmax, "dtl")
 
 
-# Every selectable 256x256 main-loop variant: (schedule, direct-to-LDS, waves).
-SCHED_VARIANTS = [(0, 0, 8), (0, 0, 4), (1, 0, 8), (0, 1, 8), (0, 1, 4), (1, 1, 8), (0, 2, 8),
-                  (1, 2, 8), (2, 1, 4), (2, 2, 4)]
+# Every selectable 256x256 main-loop variant: (schedule, direct-to-LDS, waves, block).
+SCHED_VARIANTS = [(0, 0, 8, 32), (0, 0, 4, 32), (1, 0, 8, 32), (0, 1, 8, 32), (0, 1, 4, 32),
+                  (1, 1, 8, 32), (0, 2, 8, 32), (1, 2, 8, 32), (2, 1, 4, 32), (2, 2, 4, 32),
+                  (1, 1, 8, 16), (1, 2, 8, 16)]
 
 
-@pytest.mark.parametrize("sched,dtl,waves", SCHED_VARIANTS)
+@pytest.mark.parametrize("sched,dtl,waves,mfma", SCHED_VARIANTS)
 @pytest.mark.parametrize("la,lb", LAYOUTS)
-def test_every_schedule_variant_bit_exact(sched, dtl, waves, la, lb):
+def test_every_schedule_variant_bit_exact(sched, dtl, waves, mfma, la, lb):
     if dtl == 1 and (la, lb) == ("col", "row"):
         pytest.skip("no K-contiguous operand to load directly")
     if dtl == 2 and (la, lb) == ("row", "col"):
         pytest.skip("no transposed operand")
-    if sched == 2 and dtl == 1 and (la, lb) != ("row", "col"):
-        pytest.skip("schedule 2 loads transposed operands with transposing reads (dtl 2)")
+    if (sched == 2 or mfma == 16) and dtl == 1 and (la, lb) != ("row", "col"):
+        pytest.skip("every operand direct: transposed ones with transposing reads (dtl 2)")
     from helpers import env
     M, N, K = 264, 520, 456
-    _say("sched", sched, dtl, waves, la, lb)
+    _say("sched", sched, dtl, waves, mfma, la, lb)
     inp = _inputs_int(M, N, K, la, lb, "f16", seed=97)
-    with env(DGEMM_FORCE_SCHED=sched, DGEMM_FORCE_DTL=dtl, DGEMM_FORCE_WAVES=waves):
+    with env(DGEMM_FORCE_SCHED=sched, DGEMM_FORCE_DTL=dtl, DGEMM_FORCE_WAVES=waves,
+             DGEMM_FORCE_MFMA=mfma):
         c, info = run_gpu(inp, "f16", "f32", split_k=1, force_tile="256x256", guard=16)
-    assert info["waves"] == waves and info["schedule"] == sched
+    assert info["waves"] == waves and info["schedule"] == sched and info["mfma_m"] == mfma
     assert (info["direct_lds"] != 0) == bool(dtl) and ((info["direct_lds"] & 12) != 0) == (dtl == 2)
     _, ref = reference(inp, "f16", "f32")
     assert np.array_equal(c, ref)
@@ -467,47 +472,55 @@ def _tr_bits(la, lb):
     return ((1 if la == "row" else 4) | (2 if lb == "col" else 8))
 
 
-def _tr_sched_instantiated(fmt, la, lb, sched):
-    # ping-pong with transposing reads: every layout for fp16, NT only for bf16
-    return sched == 0 or fmt == "f16" or (la, lb) == ("col", "row")
+def _tr_sched_instantiated(fmt, la, lb, sched, mfma=32):
+    # transposing reads: the pipeline (32x32x16) and the 16x16x32 ping-pong in every layout;
+    # the 32x32x16 ping-pong in every layout for fp16, NT only for bf16
+    return sched == 0 or mfma == 16 or fmt == "f16" or (la, lb) == ("col", "row")
+
+
+# (schedule, matrix-core block): the 32x32x16 ping-pong and pipeline (two K rows per 1 KiB
+# LDS block, B = 8, S = 4) and the 16x16x32 ping-pong (64-wide K-row segments, B = 64, S = 8)
+TR_SCHED = [(1, 32), (0, 32), (1, 16)]
+TR_PERM = {32: (8, 4, 64), 16: (64, 8, 64)}
 
 
 @pytest.mark.parametrize("la,lb", TR_LAYOUTS)
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
-@pytest.mark.parametrize("sched", [1, 0])
-def test_transposing_lds_reads_integer_bit_exact(la, lb, fmt, sched):
+@pytest.mark.parametrize("sched,mfma", TR_SCHED)
+def test_transposing_lds_reads_integer_bit_exact(la, lb, fmt, sched, mfma):
     # transposed operands kept in global order in padded, K-row-permuted LDS blocks and
     # transposed by ds_read_b64_tr_b16, in the ping-pong (1) and the pipeline (0) schedule;
     # ragged M, N and K
-    if not _tr_sched_instantiated(fmt, la, lb, sched):
+    if not _tr_sched_instantiated(fmt, la, lb, sched, mfma):
         pytest.skip("not instantiated")
     from helpers import env
     M, N, K = 392 + 8, 648, 200
-    _say("tr-int", la, lb, fmt, sched)
+    _say("tr-int", la, lb, fmt, sched, mfma)
     inp = _inputs_int(M, N, K, la, lb, fmt, seed=101)
-    with env(DGEMM_FORCE_DTL=2, DGEMM_FORCE_SCHED=sched):
+    with env(DGEMM_FORCE_DTL=2, DGEMM_FORCE_SCHED=sched, DGEMM_FORCE_MFMA=mfma):
         c, info = run_gpu(inp, fmt, "f32", split_k=1, force_tile="256x256", guard=64)
     assert info["direct_lds"] == _tr_bits(la, lb) and info["schedule"] == sched
-    assert (info["perm_block"], info["perm_stride"], info["lds_pad_bytes"]) == (8, 4, 64)
+    assert info["mfma_m"] == mfma
+    assert (info["perm_block"], info["perm_stride"], info["lds_pad_bytes"]) == TR_PERM[mfma]
     _, ref = reference(inp, fmt, "f32")
     assert np.array_equal(c, ref)
 
 
 @pytest.mark.parametrize("la,lb", TR_LAYOUTS)
-@pytest.mark.parametrize("sched", [1, 0])
-def test_transposing_lds_reads_split_k_and_random(la, lb, sched):
+@pytest.mark.parametrize("sched,mfma", TR_SCHED)
+def test_transposing_lds_reads_split_k_and_random(la, lb, sched, mfma):
     from helpers import env
     M, N, K = 264, 520, 1032
-    _say("tr-split", la, lb, sched)
+    _say("tr-split", la, lb, sched, mfma)
     inp = _inputs_int(M, N, K, la, lb, "f16", seed=103)
     _, ref = reference(inp, "f16", "f32")
-    with env(DGEMM_FORCE_DTL=2, DGEMM_FORCE_SCHED=sched):
+    with env(DGEMM_FORCE_DTL=2, DGEMM_FORCE_SCHED=sched, DGEMM_FORCE_MFMA=mfma):
         for sk in (1, 4):
             c, info = run_gpu(inp, "f16", "f32", split_k=sk, force_tile="256x256", guard=16)
             assert info["direct_lds"] == _tr_bits(la, lb) and info["split_k"] == sk
-            assert info["schedule"] == sched
+            assert info["schedule"] == sched and info["mfma_m"] == mfma
             assert np.array_equal(c, ref), sk
-        fmt = "bf16" if _tr_sched_instantiated("bf16", la, lb, sched) else "f16"
+        fmt = "bf16" if _tr_sched_instantiated("bf16", la, lb, sched, mfma) else "f16"
         inp = _inputs_rand(520, 392, 328, la, lb, fmt, seed=105)
         c, info = run_gpu(inp, fmt, fmt, split_k=1, force_tile="256x256", guard=16)
         assert info["schedule"] == sched
