@@ -4,17 +4,18 @@
 namespace dg {
 
 static const Variant kTable[] = {
-    // Defaults first (the planner takes the first match), all on the 8-wave ping-pong
-    // schedule: TN (both operands K-contiguous) and NT (both transposed) with 16x16x32
-    // blocks and every operand straight into LDS (NT's in 64-wide K-row segments,
-    // transposed by the LDS reads); NN and TT with 32x32x16 blocks, the K-contiguous
-    // operand straight into LDS and the transposed one through the in-register
-    // transpose. Then the alternatives: 32x32x16 blocks for TN and NT (NT transposed by
-    // the LDS reads; the in-register transpose of both measured 11-18% slower,
-    // DGEMM_FORCE_DTL=0), the single-schedule pipeline kernels (DGEMM_FORCE_SCHED=0), and
-    // NN and TT with 16x16x32 blocks and transposing reads (DGEMM_FORCE_MFMA=16).
+    // Defaults first (the planner takes the first match): the 8-wave ping-pong schedule
+    // with 16x16x32 blocks, K-contiguous operands straight into LDS; a transposed operand
+    // through the in-register transpose where the other is K-contiguous (NN, TT), both
+    // straight into LDS in 64-wide K-row segments and transposed by the LDS reads where
+    // both are transposed (NT; the in-register transpose of both measured 11-18% slower,
+    // DGEMM_FORCE_DTL=0). Then the alternatives: 32x32x16 blocks on the same schedule
+    // (DGEMM_FORCE_MFMA=32), the single-schedule pipeline kernels (DGEMM_FORCE_SCHED=0),
+    // and NN and TT with transposing reads (DGEMM_FORCE_DTL=2).
     TILE_XM(F16T, true, true, false, 256, 256, 2, 4, true, 1, 1, 16),
     TILE_XM(F16T, false, false, false, 256, 256, 2, 4, true, 1, 2, 16),
+    TILE_XM(F16T, false, true, false, 256, 256, 2, 4, true, 1, 1, 16),
+    TILE_XM(F16T, true, false, false, 256, 256, 2, 4, true, 1, 1, 16),
     TILE_LAYOUTS_PPDTL(F16T, 256, 256, 2, 4),
     TILE_LAYOUTS_PPTR(F16T, 256, 256, 2, 4),
     TILE_LAYOUTS_PP(F16T, 256, 256, 2, 4),

@@ -21,7 +21,9 @@ static const Variant kTable[] = {
     SKINNY(F16T, false, 2, 8, 2, 1),
     SKINNY(F16T, true, 4, 8, 2, 1),
     // int4 B (column-major codes), A either layout; row-major A: the ping-pong schedule with
-    // A loaded straight into LDS (column-major A: the pipeline, which measured faster)
+    // A loaded straight into LDS (column-major A: the pipeline, which measured faster). The
+    // 16x16x32 blocks keep their accumulators in VGPRs, which with the register-staged codes
+    // and scales spilled and ran 2.1x slower; int4 B stays on 32x32x16 blocks.
     TILE_X(F16T, true, true, true, 256, 256, 2, 4, true, true, 1),
     TILE(F16T, true, true, true, 256, 256, 2, 4, true),
     TILE(F16T, false, true, true, 256, 256, 2, 4, true),

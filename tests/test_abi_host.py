@@ -185,10 +185,16 @@ def test_headline_plans(fake_cus):
         assert (i["tile_m"], i["tile_n"], i["grid_x"], i["waves"]) == (192, 320, grid, 8)
         assert (i["schedule"], i["mfma_m"], i["direct_lds"], i["split_k"]) == (1, 16, 12, sk)
         assert (i["perm_block"], i["perm_stride"], i["lds_pad_bytes"]) == (64, 8, 64)
-    # the 4096^3 headline (NN, in-register transpose of A) stays on 32x32x16 blocks
+    # the 4096^3 headline (NN, in-register transpose of A) on 16x16x32 blocks; 32x32x16 on
+    # request
     p = dg.gemm_plan(4096, 4096, 4096, COL, COL, F16, F16, F16, 0)
-    assert dg.gemm_plan_query(p)["mfma_m"] == 32
+    assert dg.gemm_plan_query(p)["mfma_m"] == 16
     dg.gemm_plan_destroy(p)
+    with env(DGEMM_FORCE_MFMA=32):
+        p = dg.gemm_plan(4096, 4096, 4096, COL, COL, F16, F16, F16, 0)
+        i = dg.gemm_plan_query(p)
+        dg.gemm_plan_destroy(p)
+    assert (i["mfma_m"], i["schedule"], i["direct_lds"], i["perm_block"]) == (32, 1, 2, 64)
 
 
 @pytest.mark.parametrize("dt", [F16, BF16])
@@ -205,9 +211,8 @@ def test_default_loader_and_schedule_per_layout(fake_cus, dt, M, N, K):
         want = {(ROW, COL): (3, (1, 1), 0), (COL, COL): (6, (64, 8), 64),
                 (ROW, ROW): (9, (64, 8), 64), (COL, ROW): (12, (64, 8), 64)}
     else:
-        # TN and NT (no operand for the in-register transpose) in 16x16x32 blocks, NT's
-        # transposed operands in 64-wide K-row segments; NN and TT in 32x32x16 blocks
-        tile, mfma = (256, 256), {(ROW, COL): 16, (COL, ROW): 16, (COL, COL): 32, (ROW, ROW): 32}
+        # 16x16x32 blocks in every layout, NT's transposed operands in 64-wide K-row segments
+        tile, mfma = (256, 256), 16
         want = {(ROW, COL): (3, (1, 1), 0), (COL, COL): (2, (64, 8), 16),
                 (ROW, ROW): (1, (64, 8), 16), (COL, ROW): (12, (64, 8), 64)}
     for (la, lb), (bits, perm, pad) in want.items():
@@ -215,7 +220,7 @@ def test_default_loader_and_schedule_per_layout(fake_cus, dt, M, N, K):
         i = dg.gemm_plan_query(p)
         dg.gemm_plan_destroy(p)
         assert (i["tile_m"], i["tile_n"], i["waves"], i["schedule"]) == (*tile, 8, 1), (la, lb)
-        assert i["mfma_m"] == (mfma if isinstance(mfma, int) else mfma[(la, lb)]), (la, lb)
+        assert i["mfma_m"] == mfma, (la, lb)
         assert i["direct_lds"] == bits, (la, lb)
         assert (i["perm_block"], i["perm_stride"]) == perm, (la, lb)
         assert i["lds_pad_bytes"] == pad, (la, lb)

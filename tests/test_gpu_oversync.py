@@ -62,7 +62,8 @@ LAYOUTS = [("col", "col"), ("col", "row"), ("row", "col"), ("row", "row")]
 # (schedule, loader): loader 0 = transposed operands through registers, 1 = K-contiguous
 # operands straight into LDS, 2 = transposed operands straight into LDS, transposed by the reads
 SCHED_LOADER = [(1, 1), (1, 2), (1, 0), (0, 0), (0, 1), (0, 2), (2, 1), (2, 2)]
-# the 16x16x32 ping-pong (every operand direct) at 256x256
+# the 16x16x32 ping-pong at 256x256 (loader 1: K-contiguous operands direct, transposed
+# ones through the in-register transpose; loader 2: every operand direct)
 SCHED_LOADER16 = [(1, 1), (1, 2)]
 
 
@@ -79,8 +80,8 @@ def _served(sched, loader, la, lb, tile="256x256"):
                          [(s, l, 16) for s, l in SCHED_LOADER16])
 @pytest.mark.parametrize("la,lb", LAYOUTS)
 def test_oversynchronised_build_bit_identical(sched, loader, mfma, la, lb):
-    # (the 16x16x32 ping-pong loads every operand directly, as schedule 2 does)
-    if not _served(2 if mfma == 16 else sched, loader, la, lb):
+    # (with loader 2 the 16x16x32 ping-pong loads every operand directly, as schedule 2 does)
+    if not _served(2 if (mfma == 16 and loader == 2) else sched, loader, la, lb):
         pytest.skip("this loader serves no operand of this layout pair")
     M, N, K = 520, 264, 712   # 3 x 2 tiles of 256 x 256, ragged edges, 11 K steps + a tail
     _say("oversync", sched, loader, mfma, la, lb)

@@ -223,10 +223,9 @@ def _dtl_bits(la, lb):
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
 def test_direct_to_lds_integer_bit_exact(waves, sched, mfma, la, lb, fmt):
     # K-contiguous operands loaded straight into swizzled LDS rows, in the ping-pong (1) and
-    # the pipeline (0) schedule, in 32x32x16 and (ping-pong, TN) 16x16x32 blocks; ragged M,
-    # N and K (K = 200: the last step has one 8-wide chunk) exercise the out-of-range zero fill
-    if mfma == 16 and (la, lb) != ("row", "col"):
-        pytest.skip("16x16x32 blocks with loader 1: TN only")
+    # the pipeline (0) schedule, in 32x32x16 and (ping-pong) 16x16x32 blocks, the transposed
+    # operand of NN and TT through the in-register transpose; ragged M, N and K (K = 200: the
+    # last step has one 8-wide chunk) exercise the out-of-range zero fill
     M, N, K = 392 + 8, 648, 200
     _say("dtl-int", waves, sched, mfma, la, lb, fmt)
     inp = _inputs_int(M, N, K, la, lb, fmt, seed=91)
@@ -271,7 +270,7 @@ def test_every_schedule_variant_bit_exact(sched, dtl, waves, mfma, la, lb):
         pytest.skip("no K-contiguous operand to load directly")
     if dtl == 2 and (la, lb) == ("row", "col"):
         pytest.skip("no transposed operand")
-    if (sched == 2 or mfma == 16) and dtl == 1 and (la, lb) != ("row", "col"):
+    if sched == 2 and dtl == 1 and (la, lb) != ("row", "col"):
         pytest.skip("every operand direct: transposed ones with transposing reads (dtl 2)")
     from helpers import env
     M, N, K = 264, 520, 456
