@@ -162,7 +162,9 @@ int make_plan(Plan& p, int split_k_req) {
   p.tile_k = v.tile_k;
   p.waves = v.waves;
   p.wave_split_k = v.wave_split_k;
-  p.lds_pad = 16;
+  // padding after each row of an operand stored by the threads: 16 bytes, 32 for the 16x16x32
+  // kernels (whose transposed rows also swap chunk c to c ^ ((r >> 2) & 1))
+  p.lds_pad = (v.kernel == KERNEL_TILE && v.mfma == 16) ? 32 : 16;
   const bool transposed = (p.layout_a == 1) || (p.layout_b == 0 && p.dtype_b != DT_U4);
   // row permutation of operands transposed in registers: 64 rows, stride 8 (16-bit) or
   // 256 rows, stride 16 (fp8)

@@ -335,12 +335,19 @@ struct Slot {
 //     permutation, inv(16v + e) = 16e + v, and a row's dword offset is 36 row: the 32 lanes
 //     of one 128-byte store phase (eight v, four kg) hit dwords 36 v + kg, all different
 //     modulo 32 (and the 64 lanes of the wave all different modulo 64).
+// PITCH 160 (the 16x16x32 kernels' transposed operands): 32 bytes of padding, and in every
+// LDS row r the 16-byte chunk c is kept at position c ^ ((r >> 2) & 1). Measured with the
+// bank-conflict counter on gfx950: at the 144-byte pitch the 16-row fragment reads of a
+// 16x16x32 block (16 rows x four chunks per instruction) take two passes, at 160 bytes the
+// transposing stores do, and at 160 bytes with this chunk swap neither does (the 32-row
+// reads of 32x32x16 blocks are conflict-free at 144 bytes, which those kernels keep).
 template <int KIND, int ROWS, int THREADS, RowPerm P, int EB = 2, int PITCH = 144>
 struct Operand {
   static constexpr int BK = 128 / EB;
-  // LDS row pitch: 128 B of data plus 16 B of padding (128: no padding, a comparison
-  // variant whose fragment reads and transposed stores meet bank conflicts)
+  // LDS row pitch: 128 B of data plus 16 B (or 32 B) of padding (128: no padding, a
+  // comparison variant whose fragment reads and transposed stores meet bank conflicts)
   static constexpr int PITCH_B = PITCH;
+  static constexpr bool CSWZ = PITCH == 160;   // chunk c of row r at c ^ ((r >> 2) & 1)
   static constexpr int VPB = KIND == 2 ? 1 : 4;
   static constexpr int BLOCKS = ROWS * 2;            // blocks per K step
   static constexpr int SLOTS = (BLOCKS + THREADS - 1) / THREADS;
@@ -356,12 +363,14 @@ struct Operand {
     return true;
   }
   static_assert(es_ok(), "row permutation must step evenly inside a vector");
+  static_assert(!CSWZ || ES % 8 == 0, "chunk swap: a block's eight rows must share bit 2");
   static_assert(ROWS % 64 == 0 && ROWS % P.block == 0, "tile rows must be whole permutation blocks");
   static_assert((KIND != 1 && KIND != 2) || EB == 2, "16-bit operand kinds");
   static_assert(KIND != 3 || EB == 1, "fp8 operand kind");
   static_assert(!(PARTIAL && KIND == 2), "int4 blocks must fill every thread");
-  static_assert(PITCH == 144 || (PITCH == 128 && !PARTIAL && KIND != 2),
-                "unpadded rows: no idle lanes (they store into the padding), no int4");
+  static_assert(PITCH == 144 || (PITCH == 128 && !PARTIAL && KIND != 2) || (PITCH == 160 && KIND == 1),
+                "unpadded rows: no idle lanes (they store into the padding), no int4; the chunk "
+                "swap of 160-byte rows: transposed 16-bit operands only");
 
   // Block q of this K split: offsets, K offset and LDS base. Blocks past BLOCKS (idle
   // lanes of a partial slot) read nothing (zeros) and store them into padding bytes of
@@ -386,7 +395,10 @@ struct Operand {
       for (int j = 0; j < 4; ++j)
         s.off[j] = ok ? (uint32_t)((kb + 8 * kg + 4 * kh + j) * ld + row0 + 8 * v) * 2u : kOOB;
       s.kofs = 8 * kg + 4 * kh;
-      s.wbase = P.inv(8 * v) * PITCH_B + 16 * kg + 8 * kh;
+      // rows inv(8v) + e*ES (ES a multiple of 8) share bit 2, so one chunk position serves
+      // all eight stores of the block
+      const int r0 = P.inv(8 * v);
+      s.wbase = r0 * PITCH_B + 16 * (CSWZ ? (kg ^ ((r0 >> 2) & 1)) : kg) + 8 * kh;
     } else if constexpr (KIND == 3) {
       static_assert(ROWS % 128 == 0, "eight 16-byte vectors per store phase");
       const int h = q >> 5;
@@ -636,9 +648,14 @@ struct TileCfg {
   static_assert(LROWS >= 0 && LROWS <= 2 && (LROWS != 2 || (DTL == 0 && !U4B)),
                 "unpadded rows: a comparison variant of the register-staged kernels");
   static constexpr int PITCH = LROWS == 2 ? 128 : 144;
+  // 16x16x32 blocks read 16 rows per instruction: an operand they take transposed through
+  // registers gets 160-byte rows with a chunk swap (Operand)
+  static constexpr int PITCH_OA = (MI == 16 && !A_KC && !A_TR && LROWS == 1) ? 160 : PITCH;
+  static constexpr int PITCH_OB = (MI == 16 && !B_KC && !B_TR && !U4B && LROWS == 1) ? 160 : PITCH;
+  static constexpr bool CSWZ_A = PITCH_OA == 160, CSWZ_B = PITCH_OB == 160;
   static constexpr int KT = F8 ? 3 : 1;                  // kind of a transposed operand
-  using OpA = Operand<A_KC ? 0 : KT, MT_M, THREADS, PA, EB, PITCH>;
-  using OpB = Operand<U4B ? 2 : (B_KC ? 0 : KT), MT_N, THREADS, PB, EB, PITCH>;
+  using OpA = Operand<A_KC ? 0 : KT, MT_M, THREADS, PA, EB, PITCH_OA>;
+  using OpB = Operand<U4B ? 2 : (B_KC ? 0 : KT), MT_N, THREADS, PB, EB, PITCH_OB>;
   using DA = DtlOperand<MT_M, THREADS, EB>;
   using DB = DtlOperand<MT_N, THREADS, EB>;
   // (the 16x16x32 kernels read transposed operands from the segment layout at any width)
@@ -649,7 +666,7 @@ struct TileCfg {
   static constexpr int SB = (B_DTL || B_TR) ? 0 : OpB::SLOTS;
   // LDS row pitch in 16-byte units: 128 B of data, plus 16 B of padding for operands
   // stored by the threads (none for direct-to-LDS rows, which use the chunk swizzle).
-  static constexpr int PA16 = A_DTL ? 8 : PITCH / 16, PB16 = B_DTL ? 8 : PITCH / 16;
+  static constexpr int PA16 = A_DTL ? 8 : PITCH_OA / 16, PB16 = B_DTL ? 8 : PITCH_OB / 16;
   static constexpr int A16 = A_TR ? TA::BYTES / 16 : MT_M * PA16;
   static constexpr int B16 = B_TR ? TB::BYTES / 16 : MT_N * PB16;
   static constexpr int STAGE16 = A16 + B16;
@@ -907,8 +924,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   int a_rd16[2], b_rd16[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int ca = Cfg::A_DTL ? ((4 * h + kq) ^ dtl_swz(r16)) : 4 * h + kq;
-    const int cb = Cfg::B_DTL ? ((4 * h + kq) ^ dtl_swz(r16)) : 4 * h + kq;
+    // (16-aligned blocks: a lane's row bits below 4 are those of r16)
+    const int csa = Cfg::CSWZ_A ? ((r16 >> 2) & 1) : 0, csb = Cfg::CSWZ_B ? ((r16 >> 2) & 1) : 0;
+    const int ca = Cfg::A_DTL ? ((4 * h + kq) ^ dtl_swz(r16)) : ((4 * h + kq) ^ csa);
+    const int cb = Cfg::B_DTL ? ((4 * h + kq) ^ dtl_swz(r16)) : ((4 * h + kq) ^ csb);
     a_rd16[h] = (wm * Cfg::WT_M + r16) * PA16 + ca;
     b_rd16[h] = Cfg::A16 + (wn * Cfg::WT_N + r16) * PB16 + cb;
   }

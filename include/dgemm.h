@@ -85,7 +85,9 @@ typedef struct {
   int32_t kernel;          /* 0 = tiled kernel, 1 = skinny split-K kernel */
   int32_t tile_m, tile_n, tile_k; /* macro tile; tile_k = K elements per main-loop step */
   int32_t waves;           /* wavefronts (64 lanes) per workgroup */
-  int32_t lds_pad_bytes;   /* padding after each K-contiguous LDS row */
+  int32_t lds_pad_bytes;   /* padding after each K-contiguous LDS row of an operand stored by
+                              the threads (16; 32 with mfma_m = 16, whose transposed rows also
+                              keep 16-byte chunk c of row r at position c ^ ((r >> 2) & 1)) */
   int32_t perm_block;      /* rows per block of the LDS row permutation (1 = none) */
   int32_t perm_stride;     /* stride S of that permutation (rocm-libraries PR 2487) */
   int32_t split_k;         /* K splits across workgroups */

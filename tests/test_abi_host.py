@@ -169,7 +169,7 @@ def test_headline_plans(fake_cus):
     i = dg.gemm_plan_query(p)
     dg.gemm_plan_destroy(p)
     assert (i["tile_m"], i["tile_n"], i["split_k"], i["grid_x"]) == (256, 256, 1, 256)
-    assert (i["perm_block"], i["perm_stride"], i["lds_pad_bytes"]) == (64, 8, 16)
+    assert (i["perm_block"], i["perm_stride"], i["lds_pad_bytes"]) == (64, 8, 32)
     assert i["direct_lds"] == 2   # B (column-major, K-contiguous) goes straight to LDS
     assert i["schedule"] == 1     # two wave groups in ping-pong
     assert i["lds_bytes"] <= 160 * 1024
@@ -213,8 +213,9 @@ def test_default_loader_and_schedule_per_layout(fake_cus, dt, M, N, K):
     else:
         # 16x16x32 blocks in every layout, NT's transposed operands in 64-wide K-row segments
         tile, mfma = (256, 256), 16
-        want = {(ROW, COL): (3, (1, 1), 0), (COL, COL): (2, (64, 8), 16),
-                (ROW, ROW): (1, (64, 8), 16), (COL, ROW): (12, (64, 8), 64)}
+        # (thread-stored transposed rows of the 16x16x32 kernels: 32-byte pad and chunk swap)
+        want = {(ROW, COL): (3, (1, 1), 0), (COL, COL): (2, (64, 8), 32),
+                (ROW, ROW): (1, (64, 8), 32), (COL, ROW): (12, (64, 8), 64)}
     for (la, lb), (bits, perm, pad) in want.items():
         p = dg.gemm_plan(M, N, K, la, lb, dt, dt, dt, 1)
         i = dg.gemm_plan_query(p)
@@ -284,7 +285,7 @@ def test_direct_to_lds_plans(fake_cus, la, lb, bits):
         i = dg.gemm_plan_query(p)
         dg.gemm_plan_destroy(p)
     assert i["direct_lds"] == bits
-    assert i["lds_pad_bytes"] == (0 if bits == 3 else 16)
+    assert i["lds_pad_bytes"] == (0 if bits == 3 else 32)   # 16x16x32 kernels' transposed rows
     assert i["lds_bytes"] <= 160 * 1024
     with env(DGEMM_FORCE_DTL=1):   # both operands transposed: nothing to load directly
         with pytest.raises(dg.GemmError):
