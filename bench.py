@@ -44,8 +44,27 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_square_4096_nn.txt")
 KERNEL_DIR = os.path.join(ROOT, "dense_gemm_operand_amd", "csrc")
 
 
+# After an idle spell the GPU clock takes about 25 ms of back-to-back GEMM launches to reach
+# its steady (power-limited) level: measured 4096^3 NN batches of 20 launches after a 1 s
+# pause went 120, 138, 131, 121, ... 112 us and stayed at 111-112 us over 2000 launches.
+# Every timing here first runs this long, untimed.
+RAMP_MS = 60.0
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def ramp_up(fns, ms: float = RAMP_MS) -> None:
+    """Launch the callables in turn, 10 calls each, untimed, until `ms` of wall time have
+    passed with the GPU busy (synchronised after every turn), then synchronise."""
+    import torch
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for fn in fns:
+            for _ in range(10):
+                fn()
+        torch.cuda.synchronize()
 
 
 def kernel_sha(folder: str = KERNEL_DIR) -> str:
@@ -130,15 +149,14 @@ class Gemm:
         self.i += 1
         self.dg.gemm_run(self.plan, A, B, S, self.C, self.ws)
 
-    def time_b2b(self, n: int, warm: int = 10) -> float:
+    def time_b2b(self, n: int, warm_ms: float = RAMP_MS) -> float:
         """Average launch duration in ms: `n` back-to-back launches on the launch stream
-        bracketed by one HIP event pair (the same way the headline's timed region is taken).
-        Kernels shorter than 50 us are timed with time_graph instead, so that the host's
-        enqueue rate cannot enter the figure."""
+        bracketed by one HIP event pair (the same way the headline's timed region is taken),
+        after `warm_ms` of launches that bring the clock up from idle. Kernels shorter than
+        50 us are timed with time_graph instead, so that the host's enqueue rate cannot enter
+        the figure."""
         torch = self.torch
-        for _ in range(warm):
-            self.run()
-        torch.cuda.synchronize()
+        ramp_up([self.run], warm_ms)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(n):
@@ -273,8 +291,9 @@ def stream_context() -> dict:
 def interleaved(fns, rounds: int = 5, calls: int = 20) -> list:
     """Median ms per call of each callable, timed interleaved: rounds of `calls`
     back-to-back calls per callable, alternating, one event pair per batch, so that the
-    power-limited clock affects every callable alike."""
+    power-limited clock affects every callable alike (after a ramp-up of all of them)."""
     import torch
+    ramp_up(fns)
     t = [[] for _ in fns]
     for _ in range(rounds):
         for i, fn in enumerate(fns):
@@ -292,21 +311,22 @@ def interleaved(fns, rounds: int = 5, calls: int = 20) -> list:
 
 def loader_comparison(rounds: int = 5, calls: int = 20) -> list:
     """The two loaders for transposed operands on the same shapes, timed interleaved: the
-    in-register transpose (the default where one operand is K-contiguous; planner hook
-    DGEMM_FORCE_DTL=0 where none is) and direct-to-LDS loads in global order transposed by
-    the LDS reads (the default for NT; where one operand is K-contiguous, the fastest such
-    kernel, 16x16x32 blocks: DGEMM_FORCE_DTL=2 DGEMM_FORCE_MFMA=16). The default kernel's own
-    time is the one under "workloads"; here only the alternative's time and the ratio
-    appear."""
+    in-register transpose (the default for NN; planner hooks DGEMM_FORCE_DTL=1
+    DGEMM_FORCE_MFMA=16 for TT, DGEMM_FORCE_DTL=0 for NT) and direct-to-LDS loads in global
+    order transposed by the LDS reads (the default for TT and NT; DGEMM_FORCE_DTL=2
+    DGEMM_FORCE_MFMA=16 for NN). The default kernel's own time is the one under "workloads";
+    here only the alternative's time and the ratio appear."""
     import torch
     from dense_gemm_operand_amd import synth
     res = []
     for name, la, lb in [("square_4096", "col", "col"), ("square_4096", "row", "row"),
                          ("square_4096", "col", "row"), ("nonpow2_bf16", None, None)]:
         wl = synth.WORKLOADS[name]
-        nt = (la or wl.layout_a) == "col" and (lb or wl.layout_b) == "row"
+        pair = (la or wl.layout_a, lb or wl.layout_b)
         hs = []
-        alt_env = {"DGEMM_FORCE_DTL": "0"} if nt else {"DGEMM_FORCE_DTL": "2", "DGEMM_FORCE_MFMA": "16"}
+        alt_env = {("col", "col"): {"DGEMM_FORCE_DTL": "2", "DGEMM_FORCE_MFMA": "16"},
+                   ("row", "row"): {"DGEMM_FORCE_DTL": "1", "DGEMM_FORCE_MFMA": "16"},
+                   ("col", "row"): {"DGEMM_FORCE_DTL": "0"}}[pair]
         for envs in ({}, alt_env):   # default first, then the other loader
             os.environ.update(envs)
             try:
@@ -432,6 +452,7 @@ def int4_layout_comparison(rounds: int = 5) -> list:
         hs = [Gemm(wl, rotate_bytes=rot), Gemm(wl, rotate_bytes=rot, b_tiled=True)]
         if hbm:
             t = [[], []]
+            ramp_up([h.run for h in hs])
             for _ in range(rounds):
                 for i, h in enumerate(hs):
                     t[i].append(h.time_graph(32, 5))
@@ -551,8 +572,9 @@ def vendor_pair(la: str | None, lb: str | None, calls: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # (500 untimed launches, about 60 ms: the clock's ramp from idle is over, see RAMP_MS)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
@@ -674,7 +696,7 @@ def main():
         for dt in ("f16", "bf16"):
             aw = synth.ATTN_WORKLOADS["attn_4096"]
             at = Attn(aw, dt)
-            ms = at.time_b2b(30, warm=5)
+            ms = at.time_b2b(30)
             rec = {"workload": aw.name, "batch_heads": aw.BH, "seq_q": aw.seq_q, "seq_k": aw.seq_k,
                    "head_dim": aw.head_dim, "dtype": dt, "us": round(ms * 1e3, 2),
                    "tflops": round(at.flops / (ms * 1e-3) / 1e12, 2),

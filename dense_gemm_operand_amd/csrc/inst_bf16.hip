@@ -5,17 +5,18 @@ namespace dg {
 
 static const Variant kTable[] = {
     // Defaults first (the planner takes the first match): the 8-wave ping-pong schedule
-    // with 16x16x32 blocks, K-contiguous operands straight into LDS; a transposed operand
-    // through the in-register transpose where the other is K-contiguous (NN, TT), both
-    // straight into LDS in 64-wide K-row segments and transposed by the LDS reads where
-    // both are transposed (NT; the in-register transpose of both measured 11-18% slower,
-    // DGEMM_FORCE_DTL=0). Then the alternatives: 32x32x16 blocks on the same schedule
-    // (DGEMM_FORCE_MFMA=32), the single-schedule pipeline kernels (DGEMM_FORCE_SCHED=0),
-    // and NN and TT with transposing reads (DGEMM_FORCE_DTL=2).
+    // with 16x16x32 blocks, K-contiguous operands straight into LDS; for NN the transposed
+    // A through the in-register transpose; for TT and NT the transposed operands straight
+    // into LDS in 64-wide K-row segments and transposed by the LDS reads (measured 2-3%
+    // faster than the in-register transpose of TT's B, 11-18% faster than that of both of
+    // NT's operands, DGEMM_FORCE_DTL=0). Then the alternatives: 32x32x16 blocks on the same
+    // schedule (DGEMM_FORCE_MFMA=32), the single-schedule pipeline kernels
+    // (DGEMM_FORCE_SCHED=0), NN with transposing reads (DGEMM_FORCE_DTL=2) and TT with the
+    // in-register transpose (DGEMM_FORCE_DTL=1).
     TILE_XM(BF16T, true, true, false, 256, 256, 2, 4, true, 1, 1, 16),
     TILE_XM(BF16T, false, false, false, 256, 256, 2, 4, true, 1, 2, 16),
     TILE_XM(BF16T, false, true, false, 256, 256, 2, 4, true, 1, 1, 16),
-    TILE_XM(BF16T, true, false, false, 256, 256, 2, 4, true, 1, 1, 16),
+    TILE_XM(BF16T, true, false, false, 256, 256, 2, 4, true, 1, 2, 16),
     TILE_LAYOUTS_PPDTL(BF16T, 256, 256, 2, 4),
     TILE_X(BF16T, false, false, false, 256, 256, 2, 4, true, true, 2),
     TILE_LAYOUTS_PP(BF16T, 256, 256, 2, 4),
@@ -37,7 +38,7 @@ static const Variant kTable[] = {
     TILE_LAYOUTS_DTLTR(BF16T, 256, 256, 2, 4),
     TILE_LAYOUTS_W4(BF16T, 256, 256),
     TILE_XM(BF16T, false, true, false, 256, 256, 2, 4, true, 1, 2, 16),
-    TILE_XM(BF16T, true, false, false, 256, 256, 2, 4, true, 1, 2, 16),
+    TILE_XM(BF16T, true, false, false, 256, 256, 2, 4, true, 1, 1, 16),
 };
 
 int variants_bf16(const Variant** out) {

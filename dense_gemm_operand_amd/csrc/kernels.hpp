@@ -1457,6 +1457,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
   // than storing four-element vectors straight from the accumulators).
   constexpr bool COLS4 = epilogue_cols_ok<PB, MT_N>();
   constexpr bool RUNS16 = !COLS4 && epilogue_runs16_ok<PB, MT_N, Cfg::WT_N>();
+  // 16x16x32 blocks, B transposed in registers (64-row, stride-8 rows), one permutation block
+  // per wave: lane pairs (l, l + 32) exchange values to store whole column runs (below)
+  constexpr bool PAIR16 = MI == 16 && PB.block == 64 && PB.stride == 8 && Cfg::WT_N == 64 && TN == 4;
   auto epilogue = [&](auto dt_tag) {
     constexpr int DT = decltype(dt_tag)::value;
     using O = typename OutT<DT>::type;
@@ -1486,12 +1489,42 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
               typedef O o4 __attribute__((ext_vector_type(4)));
               o4 w = {cvt_out<DT>(v[0]), cvt_out<DT>(v[1]), cvt_out<DT>(v[2]), cvt_out<DT>(v[3])};
               *reinterpret_cast<o4*>(dst) = w;
-            } else {
+            } else if constexpr (!PAIR16) {
               // B transposed in registers: its permuted LDS rows nb + e hold logical
               // columns fwd_B(nb + e), eight apart; one element each
 #pragma unroll
               for (int e = 0; e < 4; ++e)
                 *reinterpret_cast<O*>(cl + (m - lo) * CP + PB.fwd(nb + e) * OB) = cvt_out<DT>(v[e]);
+            }
+          }
+          if constexpr (PAIR16) {
+            // B transposed in registers, 64-row stride-8 permutation, one 64-row block per
+            // wave: lane l (l < 32) holds logical columns 32(kq%2) + 8e + 2j and lane l + 32 the
+            // columns one higher (e = 0..3, block j = 0..3). Two lane swaps per block give lane
+            // l the 16 consecutive columns of e = 0, 1 and lane l + 32 those of e = 2, 3.
+            float c16[16];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+              // (copies to scalars first: a bit cast of a vector element reads element 0)
+              const float v0 = acc[i * TN + j][0], v1 = acc[i * TN + j][1];
+              const float v2 = acc[i * TN + j][2], v3 = acc[i * TN + j][3];
+              const auto s0 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v0),
+                                                               __builtin_bit_cast(unsigned, v2), false, false);
+              const auto s1 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v1),
+                                                               __builtin_bit_cast(unsigned, v3), false, false);
+              const unsigned s00 = s0[0], s01 = s0[1], s10 = s1[0], s11 = s1[1];
+              c16[2 * j] = __builtin_bit_cast(float, s00);
+              c16[2 * j + 1] = __builtin_bit_cast(float, s01);
+              c16[8 + 2 * j] = __builtin_bit_cast(float, s10);
+              c16[8 + 2 * j + 1] = __builtin_bit_cast(float, s11);
+            }
+            const int col0 = wn * 64 + 32 * (kq % 2) + 16 * (kq / 2);
+            typedef O o4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              o4 w = {cvt_out<DT>(c16[4 * q]), cvt_out<DT>(c16[4 * q + 1]), cvt_out<DT>(c16[4 * q + 2]),
+                      cvt_out<DT>(c16[4 * q + 3])};
+              *reinterpret_cast<o4*>(cl + (m - lo) * CP + (col0 + 4 * q) * OB) = w;
             }
           }
         }

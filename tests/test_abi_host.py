@@ -201,21 +201,22 @@ def test_headline_plans(fake_cus):
 @pytest.mark.parametrize("M,N,K", [(4096, 4096, 4096), (3072, 5120, 6144), (8192, 8192, 520)])
 def test_default_loader_and_schedule_per_layout(fake_cus, dt, M, N, K):
     # every layout runs the 8-wave ping-pong schedule. On 256x256 tiles K-contiguous
-    # operands go straight into LDS; a transposed operand is transposed in registers (64-row
-    # stride-8 permuted rows) unless both are transposed (NT), where both go straight into
-    # LDS in global order, in 64-wide K-row segments (B = 64, S = 8, 64 B pad), and the LDS
-    # reads transpose them. At 3072x5120 the 192x320 tile (16x16x32 blocks) takes every
+    # operands go straight into LDS; NN's transposed A is transposed in registers (64-row
+    # stride-8 permuted rows), TT's and NT's transposed operands go straight into LDS in
+    # global order, in 64-wide K-row segments (B = 64, S = 8, 64 B pad), and the LDS reads
+    # transpose them. At 3072x5120 the 192x320 tile (16x16x32 blocks) takes every
     # operand straight into LDS, transposed ones in the same segments.
     if (M, N) == (3072, 5120):
         tile, mfma = (192, 320), 16
         want = {(ROW, COL): (3, (1, 1), 0), (COL, COL): (6, (64, 8), 64),
                 (ROW, ROW): (9, (64, 8), 64), (COL, ROW): (12, (64, 8), 64)}
     else:
-        # 16x16x32 blocks in every layout, NT's transposed operands in 64-wide K-row segments
+        # 16x16x32 blocks in every layout, TT's and NT's transposed operands in 64-wide
+        # K-row segments
         tile, mfma = (256, 256), 16
         # (thread-stored transposed rows of the 16x16x32 kernels: 32-byte pad and chunk swap)
         want = {(ROW, COL): (3, (1, 1), 0), (COL, COL): (2, (64, 8), 32),
-                (ROW, ROW): (1, (64, 8), 32), (COL, ROW): (12, (64, 8), 64)}
+                (ROW, ROW): (9, (64, 8), 64), (COL, ROW): (12, (64, 8), 64)}
     for (la, lb), (bits, perm, pad) in want.items():
         p = dg.gemm_plan(M, N, K, la, lb, dt, dt, dt, 1)
         i = dg.gemm_plan_query(p)
@@ -226,12 +227,18 @@ def test_default_loader_and_schedule_per_layout(fake_cus, dt, M, N, K):
         assert (i["perm_block"], i["perm_stride"]) == perm, (la, lb)
         assert i["lds_pad_bytes"] == pad, (la, lb)
         assert i["lds_bytes"] <= 160 * 1024
-    # the in-register transpose stays selectable for NT
+    # the in-register transpose stays selectable for NT, and for TT's B on 16x16x32 blocks
     with env(DGEMM_FORCE_DTL=0):
         p = dg.gemm_plan(M, N, K, COL, ROW, dt, dt, dt, 1)
         i = dg.gemm_plan_query(p)
         dg.gemm_plan_destroy(p)
     assert (i["direct_lds"], i["schedule"], i["perm_block"]) == (0, 1, 64)
+    if tile == (256, 256):
+        with env(DGEMM_FORCE_DTL=1, DGEMM_FORCE_MFMA=16):
+            p = dg.gemm_plan(M, N, K, ROW, ROW, dt, dt, dt, 1)
+            i = dg.gemm_plan_query(p)
+            dg.gemm_plan_destroy(p)
+        assert (i["direct_lds"], i["mfma_m"], i["perm_block"], i["lds_pad_bytes"]) == (1, 16, 64, 32)
 
 
 def test_lds_row_permutation_matches_the_page_formula():
@@ -280,11 +287,11 @@ def test_query_and_destroy_null():
 
 @pytest.mark.parametrize("la,lb,bits", [(ROW, ROW, 1), (ROW, COL, 3), (COL, COL, 2)])
 def test_direct_to_lds_plans(fake_cus, la, lb, bits):
-    with env(DGEMM_FORCE_DTL=1):
+    with env(DGEMM_FORCE_DTL=1, DGEMM_FORCE_MFMA=16):
         p = dg.gemm_plan(4096, 4096, 4096, la, lb, F16, F16, F16, 0)
         i = dg.gemm_plan_query(p)
         dg.gemm_plan_destroy(p)
-    assert i["direct_lds"] == bits
+    assert (i["direct_lds"], i["mfma_m"]) == (bits, 16)
     assert i["lds_pad_bytes"] == (0 if bits == 3 else 32)   # 16x16x32 kernels' transposed rows
     assert i["lds_bytes"] <= 160 * 1024
     with env(DGEMM_FORCE_DTL=1):   # both operands transposed: nothing to load directly

@@ -112,21 +112,27 @@ def _perm_inputs(which: str, la: str, lb: str, seed: int):
 
 @pytest.mark.parametrize("which", ["A", "B"])
 @pytest.mark.parametrize("la,lb", [("col", "col"), ("col", "row"), ("row", "col"), ("row", "row")])
-@pytest.mark.parametrize("loader", ["default", "transposing_reads", "in_register"])
+@pytest.mark.parametrize("loader", ["default", "transposing_reads", "in_register", "in_register_16x16"])
 def test_full_size_permutation_every_element(which, la, lb, loader):
     # 4096^3 as the bench runs it: every element of C must be the exact permuted entry
     if loader == "transposing_reads" and la == "row" and lb == "col":
         pytest.skip("no transposed operand")
     if loader == "in_register" and (la, lb) != ("col", "row"):
-        pytest.skip("the default already transposes in registers")
+        pytest.skip("NN's default transposes in registers; TT's is the next case")
+    if loader == "in_register_16x16" and (la, lb) != ("row", "row"):
+        pytest.skip("TT's in-register transpose on 16x16x32 blocks (NN's is its default)")
     _say("full perm", which, la, lb, loader)
     inp, want = _perm_inputs(which, la, lb, seed=111 + (which == "B"))
-    force = {"default": None, "transposing_reads": 2, "in_register": 0}[loader]
-    with env(DGEMM_FORCE_DTL=force):
+    force = {"default": {}, "transposing_reads": {"DGEMM_FORCE_DTL": 2},
+             "in_register": {"DGEMM_FORCE_DTL": 0},
+             "in_register_16x16": {"DGEMM_FORCE_DTL": 1, "DGEMM_FORCE_MFMA": 16}}[loader]
+    with env(**force):
         c, info = run_gpu(inp, "f16", "f16", split_k=1, guard=16)
-    # NT (both operands transposed) takes the transposing reads by default
-    want_tr = loader == "transposing_reads" or (loader == "default" and (la, lb) == ("col", "row"))
+    # NT and TT (a transposed B) take the transposing reads by default
+    want_tr = loader == "transposing_reads" or (loader == "default" and lb == "row")
     assert ((info["direct_lds"] & 12) != 0) == want_tr
+    if loader == "in_register_16x16":
+        assert info["mfma_m"] == 16
     assert np.array_equal(c, want)
 
 

@@ -191,8 +191,8 @@ def test_no_permutation_variant_matches(dt, la, lb, no_perm):
     from helpers import env
     with env(DGEMM_NO_PERM=no_perm):
         c0, i0 = run_gpu(inp, dt, "f32", split_k=1, force_tile="256x256")
-    # the permuted in-register kernel (NT's default transposes with the LDS reads instead)
-    with env(DGEMM_FORCE_DTL=0 if (la, lb) == ("col", "row") else None):
+    # the permuted in-register kernel (NT's and TT's defaults transpose with the LDS reads)
+    with env(DGEMM_FORCE_DTL={("col", "row"): 0, ("row", "row"): 1}.get((la, lb))):
         c1, i1 = run_gpu(inp, dt, "f32", split_k=1, force_tile="256x256")
     assert i0["perm_block"] == 1 and i1["perm_block"] == 64
     assert i0["lds_pad_bytes"] == (0 if no_perm == 2 else 16)
@@ -238,17 +238,19 @@ def test_direct_to_lds_integer_bit_exact(waves, sched, mfma, la, lb, fmt):
     assert np.array_equal(c, ref)
 
 
+@pytest.mark.parametrize("mfma", [32, 16])
 @pytest.mark.parametrize("la,lb", DTL_LAYOUTS)
-def test_direct_to_lds_split_k_and_random(la, lb):
+def test_direct_to_lds_split_k_and_random(la, lb, mfma):
     from helpers import env
     M, N, K = 264, 520, 1032
-    _say("dtl-split", la, lb)
+    _say("dtl-split", la, lb, mfma)
     inp = _inputs_int(M, N, K, la, lb, "f16", seed=93)
     _, ref = reference(inp, "f16", "f32")
-    with env(DGEMM_FORCE_DTL=1):
+    with env(DGEMM_FORCE_DTL=1, DGEMM_FORCE_MFMA=mfma):
         for sk in (1, 4):
             c, info = run_gpu(inp, "f16", "f32", split_k=sk, force_tile="256x256", guard=16)
             assert info["direct_lds"] == _dtl_bits(la, lb) and info["split_k"] == sk
+            assert info["mfma_m"] == mfma
             assert np.array_equal(c, ref), sk
         inp = _inputs_rand(520, 392, 328, la, lb, "bf16", seed=95)
         c, _ = run_gpu(inp, "bf16", "bf16", split_k=1, force_tile="256x256", guard=16)
