@@ -515,12 +515,14 @@ def cpu_baselines(budget_s: float = 2.5) -> list:
 
 
 def run_workload(name: str, la, lb, steps: int):
-    """Only one workload, `steps` launches (rotating input sets for HBM-bound shapes)."""
+    """Only one workload: RAMP_MS of untimed launches, then `steps` launches (rotating input
+    sets for HBM-bound shapes). A profile of it averages the last `steps` dispatches."""
     import torch
     from dense_gemm_operand_amd import synth
     if name in synth.ATTN_WORKLOADS:
         aw = synth.ATTN_WORKLOADS[name]
         at = Attn(aw, la)   # --layout-a doubles as the attention dtype (f16 / bf16)
+        ramp_up([at.run])
         for _ in range(steps):
             at.run()
         torch.cuda.synchronize()
@@ -531,6 +533,7 @@ def run_workload(name: str, la, lb, steps: int):
     wl = synth.WORKLOADS[name]
     hbm = name in ("skinny_splitk", "int4_m16")
     g = Gemm(wl, la, lb, rotate_bytes=2 * MALL_BYTES + (64 << 20) if hbm else 0)
+    ramp_up([g.run])
     for _ in range(steps):
         g.run()
     torch.cuda.synchronize()
@@ -554,14 +557,17 @@ def copy_probe():
 
 def vendor_pair(la: str | None, lb: str | None, calls: int):
     """`calls` launches of the vendor library's product, then `calls` of this library's, on
-    the same operand memory of the 4096^3 fp16 GEMM (one layout pair, default TN)."""
+    the same operand memory of the 4096^3 fp16 GEMM (one layout pair, default TN), each after
+    RAMP_MS of untimed launches of its own."""
     import torch
     from dense_gemm_operand_amd import synth
     h = Gemm(synth.WORKLOADS["square_4096"], la or "row", lb or "col")
     mm = _vendor_mm(h)
+    ramp_up([mm])
     for _ in range(calls):
         mm()
     torch.cuda.synchronize()
+    ramp_up([h.run])
     for _ in range(calls):
         h.run()
     torch.cuda.synchronize()
