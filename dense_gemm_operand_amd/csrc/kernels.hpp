@@ -1589,7 +1589,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_tile_kernel(KArgs a) {
         if (gm >= a.M || gn >= a.N) continue;
         const char* src = cl + row * CP + cc * 16;
         if (a.c_vec && gn + 16 / OB <= a.N) {
-          *reinterpret_cast<u32x4*>(Cg + (size_t)gm * a.N + gn) = *reinterpret_cast<const u32x4*>(src);
+          // non-temporal: C is not read again here (measured 0.5-0.7% faster at 4096^3)
+          __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(src),
+                                      reinterpret_cast<u32x4*>(Cg + (size_t)gm * a.N + gn));
         } else {
 #pragma unroll
           for (int q = 0; q < 16 / OB; ++q)
