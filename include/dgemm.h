@@ -142,14 +142,16 @@ typedef struct {
  * The plan binds to the HIP device current at this call (its CU count feeds the
  * split-K search; the environment variable DGEMM_FAKE_CU_COUNT replaces the query so
  * that planning works without a device). Host only: no allocation, no launch.
- * Loader for a transposed operand: where the other operand is K-contiguous it is
- * transposed in registers with byte permutes and stored K-contiguous (Triton PR 5223).
- * Where both 16-bit operands are transposed (A column-major, B row-major) the default is
- * the other loader of the pages (rocm-libraries PR 2487): each operand goes straight into
+ * Loader for a transposed operand: for a column-major A with a column-major B (BLAS NN)
+ * and for fp8 it is transposed in registers with byte permutes and stored K-contiguous
+ * (Triton PR 5223). For a 16-bit row-major B (BLAS TT and NT) the default is the other
+ * loader of the pages (rocm-libraries PR 2487): each transposed operand goes straight into
  * LDS in global order and is transposed by the LDS reads (ds_read_b64_tr_b16). In the
- * environment, DGEMM_FORCE_DTL=2 selects the second loader for any layout (256x256 tiles)
- * and DGEMM_FORCE_DTL=0 the in-register transpose; gemm_plan_info_t.direct_lds reports
- * which was chosen.
+ * environment, DGEMM_FORCE_DTL=2 selects the second loader for any layout (256x256 tiles),
+ * DGEMM_FORCE_DTL=0 the in-register transpose of every transposed operand, and
+ * DGEMM_FORCE_DTL=1 with DGEMM_FORCE_MFMA=16 the in-register transpose beside a
+ * K-contiguous operand loaded straight into LDS; gemm_plan_info_t.direct_lds reports which
+ * was chosen.
  * On error *out is set to NULL. */
 int gemm_plan(gemm_plan_t* out, int64_t M, int64_t N, int64_t K, int layout_a, int layout_b,
               int dtype_a, int dtype_b, int dtype_c, int split_k, const gemm_quant_t* quant);
