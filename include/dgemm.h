@@ -146,7 +146,8 @@ typedef struct {
  * and for fp8 it is transposed in registers with byte permutes and stored K-contiguous
  * (Triton PR 5223). For a 16-bit row-major B (BLAS TT and NT) the default is the other
  * loader of the pages (rocm-libraries PR 2487): each transposed operand goes straight into
- * LDS in global order and is transposed by the LDS reads (ds_read_b64_tr_b16). In the
+ * LDS in global order and is transposed by the LDS reads (ds_read_b64_tr_b16), as are
+ * NN's A on the non-power-of-2 192x320 tiles (chosen where they fill the CUs). In the
  * environment, DGEMM_FORCE_DTL=2 selects the second loader for any layout (256x256 tiles),
  * DGEMM_FORCE_DTL=0 the in-register transpose of every transposed operand, and
  * DGEMM_FORCE_DTL=1 with DGEMM_FORCE_MFMA=16 the in-register transpose beside a
